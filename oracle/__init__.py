@@ -1,0 +1,107 @@
+"""fp64 CPU attention oracle (ctypes front end for ``fa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product path.  It imports nothing
+from the GPU package and the GPU package imports nothing from here; the two
+share only the seeded inputs.
+
+The arithmetic lives in ``fa_oracle.c``: exact scaled-dot-product attention
+as defined in "FlashAttention'ı Anlamak Bölüm 1", section 0.2 "Notasyon"
+(score and output equations, mask/bias term zero), evaluated row by row in
+fp64 from the bf16 input bits.  Outputs: O in fp64 (never rounded to bf16) and
+the natural-log log-sum-exp of the scaled logits per query row.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``liboracle.so`` with gcc + OpenMP (no fast-math, no FMA contraction)."""
+    tmp = _LIB_PATH + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+           "-fno-fast-math", "-ffp-contract=off", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib_handle = None
+
+
+def _lib():
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.oracle_attn_fp64.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                         ctypes.c_float, _p, _p]
+        lib.oracle_attn_fp64.restype = ctypes.c_int
+        lib.oracle_attn_rows_fp64.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                              ctypes.c_float, _p, _i64, _p, _p]
+        lib.oracle_attn_rows_fp64.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _lib_handle = lib
+    return _lib_handle
+
+
+def _shapes(Q, K, V):
+    for name, a in (("Q", Q), ("K", K), ("V", V)):
+        if a.dtype != np.uint16 or a.ndim != 4:
+            raise TypeError(f"{name} must be a 4-D uint16 array of bf16 bits, got {a.dtype} {a.shape}")
+    B, H, Nq, d = Q.shape
+    Bk, Hk, Nk, dk = K.shape
+    Bv, Hv, Nv, dv = V.shape
+    if (Bk, Hk, dk) != (B, H, d) or (Bv, Hv, Nv) != (B, H, Nk):
+        raise ValueError(f"shape mismatch Q{Q.shape} K{K.shape} V{V.shape}")
+    return B, H, Nq, Nk, d, dv
+
+
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """Full oracle: returns (O [B,H,Nq,dv] fp64, LSE [B,H,Nq] fp64)."""
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    O = np.empty((B, H, Nq, dv), dtype=np.float64)
+    LSE = np.empty((B, H, Nq), dtype=np.float64)
+    rc = _lib().oracle_attn_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                 B, H, Nq, Nk, d, dv, ctypes.c_float(scale),
+                                 O.ctypes.data, LSE.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_fp64 failed with code {rc}")
+    return O, LSE
+
+
+def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, rows: np.ndarray):
+    """Selected query rows (flat indices into [B*H*Nq]): (O [n,dv], LSE [n])."""
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n = rows.shape[0]
+    O = np.empty((n, dv), dtype=np.float64)
+    LSE = np.empty((n,), dtype=np.float64)
+    rc = _lib().oracle_attn_rows_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                      B, H, Nq, Nk, d, dv, ctypes.c_float(scale),
+                                      rows.ctypes.data, n, O.ctypes.data, LSE.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_rows_fp64 failed with code {rc}")
+    return O, LSE
+
+
+def max_threads() -> int:
+    return int(_lib().oracle_max_threads())
