@@ -1,0 +1,177 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+One step = one ``fa_fwd`` call over the whole workload (every query row of
+every head: Q-tile load, K/V loop with scores, online softmax and P V, and the
+normalised store), with Q, K, V already resident in HBM.  The default
+workload is B=2, H=16, Nq=Nk=8192, d=128 (non-causal, BF16), one of the
+sequence lengths at which the 60 %-of-peak goal is stated.
+
+Prints ONE JSON line: throughput (TFLOP/s, 4*B*H*Nq*Nk*d per call), a
+``roofline`` object for the kernel (achieved TFLOP/s from HIP events on the
+launch stream vs the MI355X dense-BF16 MFMA peak) and a ``cpu_baseline``
+object (the fp64 oracle timed on a bounded sample of the same workload on
+this host's cores).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import fa06_inputs as fi  # noqa: E402
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense BF16 matrix peak
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "b2_h16_n8192"
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+# for the current kernel on the default workload, scaled by the copy-kernel
+# calibration factor; None until measured for this kernel version.
+MEASURED_TRAFFIC_BYTES = None
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=fi.WORKLOAD_ORDER)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target wall time of the oracle sample (CPU baseline)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None):
+    import oracle
+    import torch
+    per_row_flop = 4 * w.Nk * w.d
+    total_rows = w.B * w.H * w.Nq
+    rng = np.random.default_rng(w.seed + 17)
+    # calibrate on a small sample, then size the timed sample to ~target_s
+    n0 = 64
+    rows0 = np.sort(rng.choice(total_rows, size=n0, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attention_rows(Q, K, V, w.scale, rows0)
+    dt0 = time.perf_counter() - t0
+    n = int(min(total_rows, max(n0, n0 * target_s / max(dt0, 1e-6))))
+    rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    Oo, Lo = oracle.attention_rows(Q, K, V, w.scale, rows)
+    dt = time.perf_counter() - t0
+    res = {
+        "value": n * per_row_flop / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"{n} of {total_rows} query rows of {w.name} (all {w.Nk} keys each), fp64, {dt:.1f} s",
+    }
+    parity = None
+    if o_gpu is not None:
+        idx = torch.from_numpy(rows).to(o_gpu.device)
+        og = o_gpu.view(-1, w.d)[idx].float().cpu().numpy().astype(np.float64)
+        lg = lse_gpu.view(-1)[idx].cpu().numpy().astype(np.float64)
+        dO = np.abs(og - Oo)
+        parity = {"rows": n, "max_abs_dO": float(dO.max()), "mean_abs_dO": float(dO.mean()),
+                  "max_abs_dLSE": float(np.abs(lg - Lo).max())}
+    return res, parity
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the forward pass shards "
+              "over (batch, head, q-tile) with no communication, so multi-GPU runs are not part "
+              "of this benchmark.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import flashattention_forward_06_amd as fa
+
+    w = fi.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Q, K, V = fi.make_workload(w)
+
+    def up(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(Q), up(K), up(V)
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+    lib = fa.load_library()
+    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
+
+    def step():
+        rc = fa.fa_fwd_raw(*call_args)
+        if rc != 0:
+            raise fa.FaError(rc, fa.fa_status_string(rc))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    roof = {
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "traffic": MEASURED_TRAFFIC_BYTES,
+        "kernel_ms": round(ev_ms, 4),
+    }
+    out = {
+        "metric": "fwd attention TFLOP/s (bf16, d=128, non-causal) and % of MI355X MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": False, "scale": w.scale, "seed": w.seed,
+                   "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+                   "kernel": fa.fa_build_info()},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse)
+        out["cpu_baseline"] = cb
+        out["parity_sampled"] = parity
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,135 @@
+"""MI355X (gfx950) fused attention forward: Python binding of ``libfa06.so``.
+
+``fa_fwd(q, k, v, scale=None) -> (o, lse)`` computes exact, dense, non-causal
+scaled-dot-product attention, ``O = softmax_row(scale * Q K^T) V``, plus the
+natural-log log-sum-exp of each row ("FlashAttention'ı Anlamak Bölüm 1",
+section 0.2, score and output equations without the mask term).  Tensors
+are BF16 ``[B, H, N, 128]`` on an MI355X; the work runs in the HIP kernel of
+``libfa06.so``.  This module only marshals arguments: PyTorch provides device
+memory and the current stream.  There is no fallback: if the library is
+missing or the device is not gfx950 the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libfa06.so")
+
+FA_HEAD_DIM = 128
+FA_MAX_SEQ = 1 << 23
+
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+    4: "FA_ERR_ALIAS", 5: "FA_ERR_INVALID_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH",
+}
+
+
+class FaError(RuntimeError):
+    """A non-zero status returned by the C ABI."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load ``libfa06.so`` (built in-tree by ``build.py``); raise if absent.
+
+    torch is imported first so the process has a single HIP runtime: the
+    library's dependency on ``libamdhip64.so.7`` then resolves to the copy
+    torch already loaded.
+    """
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    import torch  # noqa: F401  (loads the HIP runtime torch uses)
+
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is not built; run `python -m flashattention_forward_06_amd.build` "
+                          "or __graft_entry__.build() first")
+    lib = ctypes.CDLL(p)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_status_string.argtypes = [ctypes.c_int]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_build_info.argtypes = []
+    lib.fa_build_info.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def fa_status_string(status: int) -> str:
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def fa_build_info() -> str:
+    return load_library().fa_build_info().decode()
+
+
+def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+               B: int, H: int, Nq: int, Nk: int, d: int, scale: float, stream: int) -> int:
+    """Direct call of the C ``fa_fwd`` on raw device pointers; returns the status."""
+    return load_library().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d,
+                                 ctypes.c_float(scale), stream)
+
+
+def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None):
+    """Fused attention forward on torch tensors.
+
+    q: [B, H, Nq, 128] bf16, k and v: [B, H, Nk, 128] bf16, all contiguous on
+    the same HIP device.  ``scale`` defaults to 1/sqrt(128).  Returns
+    ``(o, lse)``: o [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional
+    ``out`` / ``lse`` tensors of those shapes receive the results.  The call
+    is enqueued on the current stream of q's device.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got shape {tuple(t.shape)}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on a HIP device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    B, H, Nq, d = q.shape
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
+    Nk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, Nq, d) or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous bf16 tensor [B, H, Nq, d] on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, Nq] on q's device")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                        B, H, Nq, Nk, d, float(scale), stream)
+    if rc != 0:
+        raise FaError(rc, fa_status_string(rc))
+    return out, lse
+
+
+__all__ = ["fa_fwd", "fa_fwd_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+           "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS"]

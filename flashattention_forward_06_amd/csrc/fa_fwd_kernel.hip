@@ -1,0 +1,352 @@
+// fa_fwd_kernel.hip -- gfx950 (CDNA4) fused attention forward kernel.
+//
+// Computes O = softmax_row(scale * Q K^T) V and the per-row log-sum-exp for
+// BF16 Q/K/V with head size 128 ("FlashAttention'ı Anlamak Bölüm 1",
+// section 0.2, score and output equations without the mask term).
+//
+// Work partition (B200 article, section "Kernel işini nasıl
+// bölümlendiriyor"): one workgroup per tile of BR query rows of one
+// (batch, head); the Q tile is loaded once; the workgroup then walks the K/V
+// sequence in tiles of BC keys, computing scores, updating the online
+// softmax state (row max and row sum) and accumulating P V in registers; the
+// accumulator is normalised once after the loop and written.
+//
+// MI355X mapping:
+//   * 4 waves per workgroup, 32 query rows per wave, 2 workgroups per CU.
+//   * Scores are produced transposed, S^T = K Q^T, with
+//     v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS, Q^T the B operand
+//     held in registers for the whole loop).  The accumulator then gives each
+//     lane one query and 16 keys, so row max / row sum are in-lane reductions
+//     plus one exchange between the two 32-lane halves, and the same
+//     registers, rounded to bf16, are directly the B operand of
+//     O^T += V^T P^T.  The key order inside an MFMA k-step is permuted
+//     consistently on both operands (the contraction does not depend on it).
+//   * V^T fragments come from the row-major V tile in LDS through
+//     ds_read_b64_tr_b16 (a transposing LDS read), so V is never transposed
+//     in memory.
+//   * K/V tiles are double buffered in LDS: the global loads of tile j+1 are
+//     issued before the MFMA/softmax work of tile j and written to the other
+//     LDS buffer after it (the 2-stage pipeline of the 5090 article's "v3").
+//   * LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled per row so the
+//     K fragment reads (ds_read_b128) and the V transposing reads are free
+//     of bank conflicts (the swizzled shared memory of the 5090 article's
+//     "v2", re-derived for the gfx950 LDS).
+//   * The softmax scale is folded into exp2 as scale*log2(e).  The running
+//     max is only raised when a row's new max exceeds it by more than
+//     RESCALE_SLACK (in log2 units); otherwise the stale max is kept, which is
+//     exact because the same max enters P, the row sum and the output.  This
+//     removes almost all O rescaling from the loop.
+//   * Global accesses use buffer resources sized to each (batch, head)
+//     slice: rows past Nq / Nk read as zero and stores past Nq are dropped,
+//     so ragged sequence lengths need no special load or store paths.
+//   * Workgroup ids are remapped so the q-tiles of one head run on the same
+//     XCD (workgroups are dispatched round-robin over the 8 XCDs), sharing
+//     that head's K/V in the XCD's L2.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernel.h"
+
+namespace fa06 {
+namespace {
+
+constexpr int D = 128;          // head size (d = d_v)
+constexpr int ROW_BYTES = D * 2; // one bf16 row
+constexpr int BR = 128;         // query rows per workgroup
+constexpr int BC = 64;          // keys per K/V tile
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = NWAVES * 64;
+constexpr int TILE_BYTES = BC * ROW_BYTES;   // one K or V tile: 16 KiB
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K + V
+constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered: 64 KiB
+constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Buffer resource: base, no stride, num_records bytes; dword3 selects the
+// 32-bit data format, which gfx9-family raw buffer accesses require.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Swizzled byte offset of 16-byte chunk `ch` of row `row` in a K or Q tile:
+// any 16 consecutive rows place a given chunk in 16 distinct bank groups.
+__device__ inline uint32_t k_swz(uint32_t row, uint32_t ch) {
+  return row * ROW_BYTES + ((ch ^ (row & 15u)) << 4);
+}
+// V tile: the transposing reads touch a 64-byte band (4 chunks) of 8 rows at
+// once; XOR-ing the band index with row%4 spreads 4 rows over the 256 bytes.
+__device__ inline uint32_t v_swz(uint32_t row, uint32_t ch) {
+  return row * ROW_BYTES + ((ch ^ ((row & 3u) << 2)) << 4);
+}
+
+__device__ inline float wave_max_halves(float x) {
+  // lanes l and l^32 hold the same query row
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float wave_min_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float wave_sum_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Copy one 64-row tile (K or V) from global (through registers) to LDS.
+struct TileRegs {
+  uintx4 v[4];
+};
+
+__device__ inline void tile_load(TileRegs& t, __amdgpu_buffer_rsrc_t r, uint32_t row0, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = tid + i * NTHREADS;
+    const uint32_t row = x >> 4, ch = x & 15u;
+    t.v[i] = buf_load16(r, (row0 + row) * ROW_BYTES + (ch << 4));
+  }
+}
+
+template <bool IS_V>
+__device__ inline void tile_store_lds(const TileRegs& t, char* lds, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t x = tid + i * NTHREADS;
+    const uint32_t row = x >> 4, ch = x & 15u;
+    const uint32_t off = IS_V ? v_swz(row, ch) : k_swz(row, ch);
+    *reinterpret_cast<uintx4*>(lds + off) = t.v[i];
+  }
+}
+
+template <bool NEG_SCALE>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
+fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+              const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+              int Nq, int Nk, int n_qtiles, float c_log2) {
+  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;   // query column of the S^T / O^T accumulators
+  const int h = lane >> 5;   // half of the wave
+
+  // XCD-aware remap: consecutive logical tiles (same head) go to one XCD.
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  const int nfull = nblk & ~7;
+  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+  const int bh = bid / n_qtiles;
+  const int qt = bid - bh * n_qtiles;
+  const int q0 = qt * BR;
+
+  const size_t head_q = (size_t)bh * (size_t)Nq * D;
+  const size_t head_k = (size_t)bh * (size_t)Nk * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * ROW_BYTES);
+
+  // ---- Q tile: coalesced 16-byte loads -> swizzled LDS -> B-operand registers.
+  {
+    char* qs = smem + STAGE_BYTES;  // stage 1 is free until the loop starts
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t x = tid + i * NTHREADS;
+      const uint32_t row = x >> 4, ch = x & 15u;
+      const uintx4 v = buf_load16(rq, (q0 + row) * ROW_BYTES + (ch << 4));
+      *reinterpret_cast<uintx4*>(qs + k_swz(row, ch)) = v;
+    }
+  }
+  TileRegs kr, vr;
+  tile_load(kr, rk, 0, tid);
+  tile_load(vr, rv, 0, tid);
+  tile_store_lds<false>(kr, smem, tid);
+  tile_store_lds<true>(vr, smem + TILE_BYTES, tid);
+  __syncthreads();
+
+  bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
+  {
+    const char* qs = smem + STAGE_BYTES;
+    const uint32_t row = wave * 32 + c;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(qs + k_swz(row, 2 * t + h)));
+  }
+  __syncthreads();  // stage 1 is overwritten by the first prefetch
+
+  floatx16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = floatx16{};
+  float m_run = -__builtin_inff();  // running max, log2 units, per query
+  float l_run = 0.0f;               // partial row sum of this lane's keys
+
+  const int n_tiles = (Nk + BC - 1) / BC;
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    const char* ks = smem + stage * STAGE_BYTES;
+    const char* vs = ks + TILE_BYTES;
+    const bool has_next = j + 1 < n_tiles;
+    if (has_next) {
+      tile_load(kr, rk, (j + 1) * BC, tid);
+      tile_load(vr, rv, (j + 1) * BC, tid);
+    }
+
+    // ---- S^T = K Q^T for two 32-key blocks.
+    floatx16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = floatx16{};
+      const uint32_t row = kb * 32 + c;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + k_swz(row, 2 * t + h)));
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[t], s[kb], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax (this lane: one query, 32 keys).
+    const bool last_partial = (j == n_tiles - 1) && (Nk - j * BC < BC);
+    const int valid = Nk - j * BC;
+    if (last_partial) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= valid) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
+        }
+    }
+    float ext = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
+    ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
+    const float m_tile = ext * c_log2;
+    if (__ballot(m_tile > m_run + RESCALE_SLACK) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    }
+    bf16x8 pb[4];  // B operand of O^T += V^T P^T, one per 16-key step
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
+        if (last_partial) {
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= valid) p = 0.0f;
+        }
+        lsum += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    l_run += lsum;
+
+    // ---- O^T += V^T P^T : 4 d-blocks x 4 key steps.
+    {
+      const int g = lane >> 4;          // 16-lane group
+      const int i16 = lane & 15;
+      const int sub = i16 >> 2;         // which of the 4 keys this lane addresses
+      const int q4 = i16 & 3;           // which 4-column piece of the 16 columns
+      const int hh = g >> 1;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        const int d0 = cb * 32 + (g & 1) * 16 + q4 * 4;  // first of 4 d columns
+        const uint32_t ch = (uint32_t)d0 >> 3;
+        const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
+#pragma unroll
+        for (int ks4 = 0; ks4 < 4; ++ks4) {
+          const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
+          const uint32_t r1 = r0 + 8;
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r0, ch) + within));
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r1, ch) + within));
+          // move the two 4-element results as whole dwords (no per-element
+          // extraction): a = {lo[0..3], hi[0..3]}
+          const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
+          const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, uintx4{lo2.x, lo2.y, hi2.x, hi2.y});
+          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks4], oacc[cb], 0, 0, 0);
+        }
+      }
+    }
+
+    if (has_next) {
+      char* kn = smem + (stage ^ 1) * STAGE_BYTES;
+      tile_store_lds<false>(kr, kn, tid);
+      tile_store_lds<true>(vr, kn + TILE_BYTES, tid);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
+  const float l_tot = wave_sum_halves(l_run);
+  const float inv_l = 1.0f / l_tot;
+  const int q = q0 + wave * 32 + c;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = cb * 32 + g4 * 8 + 4 * h;
+      uint32_t w0, w1;
+      {
+        const __bf16 a0 = (__bf16)(oacc[cb][4 * g4 + 0] * inv_l);
+        const __bf16 a1 = (__bf16)(oacc[cb][4 * g4 + 1] * inv_l);
+        const __bf16 a2 = (__bf16)(oacc[cb][4 * g4 + 2] * inv_l);
+        const __bf16 a3 = (__bf16)(oacc[cb][4 * g4 + 3] * inv_l);
+        w0 = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        w1 = (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16);
+      }
+      __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, ro, (uint32_t)q * ROW_BYTES + d * 2, 0, 0);
+    }
+  if (h == 0 && q < Nq) {
+    const float ln2 = 0.69314718055994530942f;
+    LSE[(size_t)bh * Nq + q] = (m_run + __log2f(l_tot)) * ln2;
+  }
+}
+
+}  // namespace
+
+int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                  int64_t BH, int64_t Nq, int64_t Nk, float scale, hipStream_t stream) {
+  const int n_qtiles = (int)((Nq + BR - 1) / BR);
+  const int64_t nblk = BH * n_qtiles;
+  const float c_log2 = (float)((double)scale * 1.4426950408889634074);
+  const uint16_t* q = static_cast<const uint16_t*>(Q);
+  const uint16_t* k = static_cast<const uint16_t*>(K);
+  const uint16_t* v = static_cast<const uint16_t*>(V);
+  uint16_t* o = static_cast<uint16_t*>(O);
+  int nq = (int)Nq, nk = (int)Nk;
+  void* args[] = {&q, &k, &v, &o, &LSE, &nq, &nk, (void*)&n_qtiles, (void*)&c_log2};
+  const void* fn = scale < 0.0f ? (const void*)&fa_fwd_kernel<true> : (const void*)&fa_fwd_kernel<false>;
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+const char* kernel_config_string() {
+  return "gfx950 fa_fwd v1: BR=128 (4 waves x 32 rows), BC=64, 2-stage LDS K/V, "
+         "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16";
+}
+
+}  // namespace fa06

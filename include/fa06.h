@@ -1,0 +1,100 @@
+/*
+ * fa06.h -- C ABI of the MI355X (gfx950) fused attention forward pass.
+ *
+ * One operation: exact, dense, non-causal scaled-dot-product attention,
+ *
+ *     O = softmax_row(scale * Q K^T) V,    LSE_i = ln sum_j exp(scale * q_i . k_j)
+ *
+ * as defined by the score and output equations of "FlashAttention'ı Anlamak
+ * Bölüm 1" (section 0.2 "Notasyon"), with the optional mask/bias term absent
+ * (the B200 article's scope: dense, non-causal, head size 128, BF16).  It is
+ * computed the way the B200 article's section "Kernel işini nasıl
+ * bölümlendiriyor" partitions it: one workgroup per tile of output rows, the
+ * Q tile loaded once, a loop over K/V tiles with an online softmax, and the
+ * output normalised once at the end.  The result is exact up to
+ * floating-point order (BF16 inputs, fp32 accumulation, BF16 output).
+ *
+ * Layout: Q, K, V and O share the [batch, heads, sequence, head_dim] shape
+ * of that same section, row-major and contiguous:
+ *     Q [B, H, Nq, d]   K [B, H, Nk, d]   V [B, H, Nk, d]   O [B, H, Nq, d]
+ *     LSE [B, H, Nq]
+ *
+ * No symbol here takes or returns a framework type; every buffer is a plain
+ * device pointer.
+ */
+#ifndef FA06_H
+#define FA06_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by fa_fwd. */
+typedef enum fa_status {
+    FA_OK = 0,
+    FA_ERR_NULL_POINTER = 1,  /* a pointer to a non-empty buffer is NULL          */
+    FA_ERR_INVALID_SHAPE = 2, /* B, H or Nq negative, Nk < 1, or sizes overflow    */
+    FA_ERR_UNSUPPORTED = 3,   /* d != 128, misaligned pointer, or N above FA_MAX_SEQ */
+    FA_ERR_ALIAS = 4,         /* O or LSE overlaps Q, K, V or each other           */
+    FA_ERR_INVALID_SCALE = 5, /* scale is NaN or infinite                          */
+    FA_ERR_DEVICE = 6,        /* no HIP device, or the current device is not gfx950 */
+    FA_ERR_LAUNCH = 7         /* the kernel launch itself failed                   */
+} fa_status;
+
+/* Head dimension the kernel is built for (d and d_v). */
+#define FA_HEAD_DIM 128
+/* Largest Nq or Nk accepted (each per-head slice stays below 2 GiB). */
+#define FA_MAX_SEQ (1LL << 23)
+
+/*
+ * fa_fwd -- fused attention forward.
+ *
+ *   Q, K, V  device pointers to bf16 bit patterns (uint16), layout above,
+ *            16-byte aligned.  Read only.
+ *   O        device pointer, bf16 [B, H, Nq, d], 16-byte aligned.  Written:
+ *            O = P V with P the row softmax, rounded to nearest even.
+ *   LSE      device pointer, fp32 [B, H, Nq], 4-byte aligned.  Written: the
+ *            natural-log log-sum-exp of the scaled logits of each query row,
+ *            the quantity a backward pass needs to recompute P.
+ *   B, H     batch and heads (>= 0).
+ *   Nq, Nk   query and key/value sequence lengths: Nq >= 0, Nk >= 1 (the
+ *            softmax of an empty row is undefined).  Any value up to
+ *            FA_MAX_SEQ; no multiple of a tile size is required.
+ *   d        head dimension; must equal FA_HEAD_DIM.
+ *   scale    finite multiplier of Q K^T (1/sqrt(d) for standard attention;
+ *            zero and negative values are accepted).
+ *   stream   hipStream_t to enqueue on; NULL is the default stream.
+ *
+ * Ownership: the caller allocates and owns every buffer; the library keeps no
+ * pointer after returning and allocates no device memory.
+ *
+ * Execution: asynchronous on `stream`; the function never synchronises.  The
+ * outputs are valid once the caller has synchronised the stream.  It
+ * launches one kernel, is reentrant, and calls on different streams may run
+ * concurrently.
+ *
+ * Errors: arguments are validated before any HIP call, shapes first, then
+ * pointers (a pointer may be NULL only when its buffer holds zero bytes, as
+ * frameworks hand out for empty tensors); on a non-zero return nothing is
+ * launched and O and LSE are untouched.  B*H*Nq == 0 is a no-op
+ * returning FA_OK.  NaN or Inf inside the inputs is not checked and
+ * propagates as IEEE arithmetic does.  Faults during execution surface at the
+ * caller's next synchronisation of the stream.
+ */
+int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+           float scale, void *stream);
+
+/* fa_status_string -- static, NUL-terminated description of a status code. */
+const char *fa_status_string(int status);
+
+/* fa_build_info -- static string naming the kernel's tile configuration. */
+const char *fa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA06_H */

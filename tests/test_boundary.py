@@ -1,0 +1,93 @@
+"""The C-ABI library on the CPU: it loads, exports what include/fa06.h
+declares, and rejects bad arguments before any HIP call (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flashattention_forward_06_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa06.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = fa.load_library()
+    names = declared_functions()
+    assert names == ["fa_build_info", "fa_fwd", "fa_status_string"]
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
+
+
+def test_status_strings():
+    for code, name in fa.STATUS.items():
+        assert fa.fa_status_string(code).startswith(name)
+    assert "unknown" in fa.fa_status_string(99)
+    assert "gfx950" in fa.fa_build_info()
+
+
+# Fake, well-aligned addresses: never dereferenced, because every call below
+# fails validation before the library touches HIP.
+Qp, Kp, Vp = 0x10000000, 0x20000000, 0x30000000
+Op, Lp = 0x40000000, 0x50000000
+GOOD = dict(B=1, H=2, Nq=256, Nk=256, d=128, scale=0.088)
+
+
+def call(q=Qp, k=Kp, v=Vp, o=Op, lse=Lp, **kw):
+    a = {**GOOD, **kw}
+    return fa.fa_fwd_raw(q, k, v, o, lse, a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
+    (dict(B=-1), 2), (dict(H=-1), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-5), 2),
+    (dict(B=1 << 40, H=1 << 40), 2),
+    (dict(d=64), 3), (dict(d=256), 3), (dict(Nq=(1 << 23) + 1), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(q=Qp + 8), 3), (dict(k=Kp + 2), 3), (dict(v=Vp + 4), 3), (dict(o=Op + 8), 3), (dict(lse=Lp + 2), 3),
+    (dict(o=Qp), 4), (dict(o=Kp + 256), 4), (dict(lse=Vp + 1024), 4), (dict(lse=Op + 4096), 4),
+    (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=float("-inf")), 5),
+])
+def test_validation_codes(kw, code):
+    assert call(**kw) == code
+
+
+def test_empty_problem_is_noop():
+    # B*H*Nq == 0 returns success without touching the device
+    assert call(Nq=0) == 0
+    assert call(B=0) == 0
+    assert call(H=0) == 0
+    # empty buffers may come with NULL pointers (torch's empty tensors do)
+    assert call(Nq=0, q=0, o=0, lse=0) == 0
+    assert call(B=0, q=0, k=0, v=0, o=0, lse=0) == 0
+    # but K and V are not empty when Nq == 0
+    assert call(Nq=0, k=0) == 1
+
+
+def test_no_device_reports_device_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this case is for hosts without one")
+    assert call() == 6
+
+
+def test_python_wrapper_type_checks():
+    import torch
+    x = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        fa.fa_fwd(x.float(), x, x)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x[0], x, x)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x)  # CPU tensors are rejected
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError):
+        fa.load_library(str(tmp_path / "nope.so"))

