@@ -48,7 +48,32 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample (CPU baseline)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="instead of attention, run a plain copy kernel (256 MiB read + 256 MiB "
+                        "written per launch) to calibrate the HBM byte counters")
     return p.parse_args()
+
+
+def calibrate_copy(args):
+    """Plain streaming kernel of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+    n = 64 << 20  # fp32 elements: 256 MiB each way
+    x = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(args.warmup):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(args.steps):
+        torch.neg(x, out=y)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    print(json.dumps({"calibration": "copy kernel (torch.neg, fp32)", "bytes_read": 4 * n,
+                      "bytes_written": 4 * n, "kernel_ms": round(ms, 4),
+                      "GB_per_s": round(8 * n / ms / 1e6, 1), "steps": args.steps}), flush=True)
 
 
 def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None):
@@ -93,6 +118,9 @@ def main():
               "over (batch, head, q-tile) with no communication, so multi-GPU runs are not part "
               "of this benchmark.", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args)
+        return
     import torch
     import flashattention_forward_06_amd as fa
 

@@ -24,9 +24,10 @@
 //   * V^T fragments come from the row-major V tile in LDS through
 //     ds_read_b64_tr_b16 (a transposing LDS read), so V is never transposed
 //     in memory.
-//   * K/V tiles are double buffered in LDS: the global loads of tile j+1 are
-//     issued before the MFMA/softmax work of tile j and written to the other
-//     LDS buffer after it (the 2-stage pipeline of the 5090 article's "v3").
+//   * K/V tiles are double buffered in LDS: tile j+1 is copied global -> LDS
+//     directly (buffer loads with the LDS destination, no registers) into
+//     the other buffer while tile j is computed (the 2-stage pipeline of the
+//     5090 article's "v3").
 //   * LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled per row so the
 //     K fragment reads (ds_read_b128) and the V transposing reads are free
 //     of bank conflicts (the swizzled shared memory of the 5090 article's
@@ -45,6 +46,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fa_kernel.h"
 
@@ -75,8 +78,8 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+__device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }
 
 // Swizzled byte offset of 16-byte chunk `ch` of row `row` in a K or Q tile:
@@ -104,30 +107,30 @@ __device__ inline float wave_sum_halves(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// Copy one 64-row tile (K or V) from global (through registers) to LDS.
-struct TileRegs {
-  uintx4 v[4];
-};
-
-__device__ inline void tile_load(TileRegs& t, __amdgpu_buffer_rsrc_t r, uint32_t row0, int tid) {
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane L of a wave
+// writes its 16 bytes at lds_base + 16*L, so each instruction fills 1 KiB of
+// LDS linearly.  The swizzle is applied on the source side: the lane that
+// fills physical chunk P of row r loads logical chunk P ^ f(r).
+// `rows` rows starting at global row `row0` (scalar) go to `lds`; every wave
+// issues rows*16/64/NWAVES instructions.
+template <int ROWS, bool IS_V>
+__device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * ROW_BYTES);
+  constexpr int N_INST = ROWS * 16 / 64 / NWAVES;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = tid + i * NTHREADS;
-    const uint32_t row = x >> 4, ch = x & 15u;
-    t.v[i] = buf_load16(r, (row0 + row) * ROW_BYTES + (ch << 4));
+  for (int i = 0; i < N_INST; ++i) {
+    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block (4 rows)
+    const uint32_t row = blk * 4 + ((uint32_t)lane >> 4);
+    const uint32_t pos = (uint32_t)lane & 15u;                // physical chunk in the row
+    const uint32_t ch = IS_V ? (pos ^ ((row & 3u) << 2)) : (pos ^ (row & 15u));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)((lds_char*)lds + blk * 1024u), 16,
+        row * ROW_BYTES + (ch << 4), soff, 0, 0);
   }
 }
 
-template <bool IS_V>
-__device__ inline void tile_store_lds(const TileRegs& t, char* lds, int tid) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t x = tid + i * NTHREADS;
-    const uint32_t row = x >> 4, ch = x & 15u;
-    const uint32_t off = IS_V ? v_swz(row, ch) : k_swz(row, ch);
-    *reinterpret_cast<uintx4*>(lds + off) = t.v[i];
-  }
-}
+// Wait until this wave's outstanding global loads (incl. LDS-direct) landed.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <bool NEG_SCALE>
 __global__ void __launch_bounds__(NTHREADS)
@@ -159,22 +162,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k, (uint32_t)Nk * ROW_BYTES);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * ROW_BYTES);
 
-  // ---- Q tile: coalesced 16-byte loads -> swizzled LDS -> B-operand registers.
-  {
-    char* qs = smem + STAGE_BYTES;  // stage 1 is free until the loop starts
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t x = tid + i * NTHREADS;
-      const uint32_t row = x >> 4, ch = x & 15u;
-      const uintx4 v = buf_load16(rq, (q0 + row) * ROW_BYTES + (ch << 4));
-      *reinterpret_cast<uintx4*>(qs + k_swz(row, ch)) = v;
-    }
-  }
-  TileRegs kr, vr;
-  tile_load(kr, rk, 0, tid);
-  tile_load(vr, rv, 0, tid);
-  tile_store_lds<false>(kr, smem, tid);
-  tile_store_lds<true>(vr, smem + TILE_BYTES, tid);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // ---- Q tile (into stage 1, free until the loop starts) and K/V tile 0.
+  tile_to_lds<BR, false>(rq, q0, smem + STAGE_BYTES, wave_u, lane);
+  tile_to_lds<BC, false>(rk, 0, smem, wave_u, lane);
+  tile_to_lds<BC, true>(rv, 0, smem + TILE_BYTES, wave_u, lane);
+  wait_vmem();
   __syncthreads();
 
   bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
@@ -193,15 +186,20 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_run = -__builtin_inff();  // running max, log2 units, per query
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
-  const int n_tiles = (Nk + BC - 1) / BC;
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
+  const int n_full = Nk / BC;                // tiles with BC valid keys
+  const int n_tiles = n_full + (Nk % BC != 0);
+
+  // One K/V tile: scores, online softmax, P V, next tile's prefetch.
+  // MASK is true only for a final partial tile (keys >= Nk masked out).
+  auto tile_step = [&](int j, auto mask_tag, auto stage_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int stage = decltype(stage_tag)::value;  // == j & 1
     const char* ks = smem + stage * STAGE_BYTES;
     const char* vs = ks + TILE_BYTES;
-    const bool has_next = j + 1 < n_tiles;
-    if (has_next) {
-      tile_load(kr, rk, (j + 1) * BC, tid);
-      tile_load(vr, rv, (j + 1) * BC, tid);
+    if (j + 1 < n_tiles) {
+      char* kn = smem + (stage ^ 1) * STAGE_BYTES;
+      tile_to_lds<BC, false>(rk, (j + 1) * BC, kn, wave_u, lane);
+      tile_to_lds<BC, true>(rv, (j + 1) * BC, kn + TILE_BYTES, wave_u, lane);
     }
 
     // ---- S^T = K Q^T for two 32-key blocks.
@@ -218,9 +216,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
 
     // ---- online softmax (this lane: one query, 32 keys).
-    const bool last_partial = (j == n_tiles - 1) && (Nk - j * BC < BC);
-    const int valid = Nk - j * BC;
-    if (last_partial) {
+    const int valid = Nk - j * BC;  // only read when MASK
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -253,7 +250,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
-        if (last_partial) {
+        if constexpr (MASK) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (key >= valid) p = 0.0f;
         }
@@ -292,12 +289,26 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       }
     }
 
-    if (has_next) {
-      char* kn = smem + (stage ^ 1) * STAGE_BYTES;
-      tile_store_lds<false>(kr, kn, tid);
-      tile_store_lds<true>(vr, kn + TILE_BYTES, tid);
-    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  int j = 0;
+  for (; j + 1 < n_full; j += 2) {
+    tile_step(j, std::false_type{}, S0{});
+    tile_step(j + 1, std::false_type{}, S1{});
+  }
+  if (j < n_full) {
+    tile_step(j, std::false_type{}, S0{});
+    ++j;
+  }
+  if (n_tiles > n_full) {
+    if (j & 1)
+      tile_step(j, std::true_type{}, S1{});
+    else
+      tile_step(j, std::true_type{}, S0{});
   }
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
@@ -345,7 +356,7 @@ int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v1: BR=128 (4 waves x 32 rows), BC=64, 2-stage LDS K/V, "
+  return "gfx950 fa_fwd v2: BR=128 (4 waves x 32 rows), BC=64, 2-stage direct-to-LDS K/V, "
          "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16";
 }
 
