@@ -163,22 +163,34 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * ROW_BYTES);
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // ---- Q tile (into stage 1, free until the loop starts) and K/V tile 0.
-  tile_to_lds<BR, false>(rq, q0, smem + STAGE_BYTES, wave_u, lane);
-  tile_to_lds<BC, false>(rk, 0, smem, wave_u, lane);
-  tile_to_lds<BC, true>(rv, 0, smem + TILE_BYTES, wave_u, lane);
+  const int n_full = Nk / BC;                 // tiles with BC valid keys
+  const int n_tiles = n_full + (Nk % BC != 0);
+  const bool tail = n_tiles > n_full;
+
+  // LDS: K buffers at [0, 32K), V buffers at [32K, 64K).  K runs one tile
+  // ahead of V: while tile j's P V is accumulated, tile j+1's scores are
+  // computed, so K(j+1) and V(j) are resident together.
+  char* const kbuf0 = smem;
+  char* const vbuf0 = smem + 2 * TILE_BYTES;
+  auto kbuf = [&](int i) { return kbuf0 + i * TILE_BYTES; };
+  auto vbuf = [&](int i) { return vbuf0 + i * TILE_BYTES; };
+
+  // ---- prologue: Q (staged in the V buffers), K(0), K(1).
+  tile_to_lds<BR, false>(rq, q0, vbuf0, wave_u, lane);
+  tile_to_lds<BC, false>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, false>(rk, BC, kbuf(1), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
   bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
   {
-    const char* qs = smem + STAGE_BYTES;
     const uint32_t row = wave * 32 + c;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(qs + k_swz(row, 2 * t + h)));
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(vbuf0 + k_swz(row, 2 * t + h)));
   }
-  __syncthreads();  // stage 1 is overwritten by the first prefetch
+  __syncthreads();  // the V buffers are reused from here on
+  tile_to_lds<BC, true>(rv, 0, vbuf(0), wave_u, lane);
 
   floatx16 oacc[4];
 #pragma unroll
@@ -186,24 +198,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_run = -__builtin_inff();  // running max, log2 units, per query
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
-  const int n_full = Nk / BC;                // tiles with BC valid keys
-  const int n_tiles = n_full + (Nk % BC != 0);
-
-  // One K/V tile: scores, online softmax, P V, next tile's prefetch.
-  // MASK is true only for a final partial tile (keys >= Nk masked out).
-  auto tile_step = [&](int j, auto mask_tag, auto stage_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int stage = decltype(stage_tag)::value;  // == j & 1
-    const char* ks = smem + stage * STAGE_BYTES;
-    const char* vs = ks + TILE_BYTES;
-    if (j + 1 < n_tiles) {
-      char* kn = smem + (stage ^ 1) * STAGE_BYTES;
-      tile_to_lds<BC, false>(rk, (j + 1) * BC, kn, wave_u, lane);
-      tile_to_lds<BC, true>(rv, (j + 1) * BC, kn + TILE_BYTES, wave_u, lane);
-    }
-
-    // ---- S^T = K Q^T for two 32-key blocks.
-    floatx16 s[2];
+  // S^T = K Q^T for the 64 keys of one K buffer (two 32-key blocks).
+  auto scores = [&](const char* ks, floatx16 (&s)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = floatx16{};
@@ -214,9 +210,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[t], s[kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- online softmax (this lane: one query, 32 keys).
-    const int valid = Nk - j * BC;  // only read when MASK
+  // Online softmax of one tile's scores -> P (bf16, B operand of the P V
+  // product).  Branch free: the decision to raise the running max is wave
+  // uniform (ballot); returns the factor the output accumulator must be
+  // multiplied by before this tile's P V is added (1 when unchanged).
+  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pb)[4], int valid, auto mask_tag, bool& rescale) -> float {
+    constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -233,17 +234,10 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
     ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
     const float m_tile = ext * c_log2;
-    if (__ballot(m_tile > m_run + RESCALE_SLACK) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-    }
-    bf16x8 pb[4];  // B operand of O^T += V^T P^T, one per 16-key step
+    rescale = __ballot(m_tile > m_run + RESCALE_SLACK) != 0;
+    const float m_new = rescale ? fmaxf(m_run, m_tile) : m_run;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -257,59 +251,115 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
-    l_run += lsum;
-
-    // ---- O^T += V^T P^T : 4 d-blocks x 4 key steps.
-    {
-      const int g = lane >> 4;          // 16-lane group
-      const int i16 = lane & 15;
-      const int sub = i16 >> 2;         // which of the 4 keys this lane addresses
-      const int q4 = i16 & 3;           // which 4-column piece of the 16 columns
-      const int hh = g >> 1;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const int d0 = cb * 32 + (g & 1) * 16 + q4 * 4;  // first of 4 d columns
-        const uint32_t ch = (uint32_t)d0 >> 3;
-        const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
-#pragma unroll
-        for (int ks4 = 0; ks4 < 4; ++ks4) {
-          const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
-          const uint32_t r1 = r0 + 8;
-          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r0, ch) + within));
-          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r1, ch) + within));
-          // move the two 4-element results as whole dwords (no per-element
-          // extraction): a = {lo[0..3], hi[0..3]}
-          const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
-          const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, uintx4{lo2.x, lo2.y, hi2.x, hi2.y});
-          oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks4], oacc[cb], 0, 0, 0);
-        }
-      }
-    }
-
-    wait_vmem();
-    __syncthreads();
+    l_run = l_run * alpha + lsum;
+    return alpha;
   };
 
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  int j = 0;
-  for (; j + 1 < n_full; j += 2) {
-    tile_step(j, std::false_type{}, S0{});
-    tile_step(j + 1, std::false_type{}, S1{});
+  // O^T += V^T P^T for the 64 keys of one V buffer: 4 d-blocks x 4 key steps.
+  auto accumulate = [&](const char* vs, const bf16x8 (&pb)[4]) {
+    const int g = lane >> 4;          // 16-lane group
+    const int i16 = lane & 15;
+    const int sub = i16 >> 2;         // which of the 4 keys this lane addresses
+    const int q4 = i16 & 3;           // which 4-column piece of the 16 columns
+    const int hh = g >> 1;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int d0 = cb * 32 + (g & 1) * 16 + q4 * 4;  // first of 4 d columns
+      const uint32_t ch = (uint32_t)d0 >> 3;
+      const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
+#pragma unroll
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
+        const uint32_t r1 = r0 + 8;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r0, ch) + within));
+        const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r1, ch) + within));
+        // move the two 4-element results as whole dwords (no per-element
+        // extraction): a = {lo[0..3], hi[0..3]}
+        const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
+        const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, uintx4{lo2.x, lo2.y, hi2.x, hi2.y});
+        oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks4], oacc[cb], 0, 0, 0);
+      }
+    }
+  };
+
+  auto rescale_o = [&](float alpha) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+  };
+
+  // ---- tile 0: scores and softmax before the loop.
+  bf16x8 pb[4];
+  {
+    floatx16 s[2];
+    scores(kbuf(0), s);
+    bool rs;
+    float alpha;
+    if (n_tiles == 1 && tail)
+      alpha = softmax(s, pb, Nk, std::true_type{}, rs);
+    else
+      alpha = softmax(s, pb, Nk, std::false_type{}, rs);
+    (void)alpha;  // O is still zero
   }
-  if (j < n_full) {
-    tile_step(j, std::false_type{}, S0{});
+  wait_vmem();
+  __syncthreads();
+
+  // Iteration j: P(j) V(j) accumulated while S(j+1) is computed and turned
+  // into P(j+1).  On entry K(j+1) is in kbuf((j+1)&1), V(j) in vbuf(j&1);
+  // the iteration prefetches K(j+2) into kbuf(j&1) and V(j+1) into
+  // vbuf((j+1)&1), whose previous contents were consumed before the last
+  // barrier.
+  auto iteration = [&](int j, auto par_tag, auto has_next_tag, auto mask_next_tag) {
+    constexpr int P = decltype(par_tag)::value;  // == j & 1
+    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
+    if (j + 2 < n_tiles) tile_to_lds<BC, false>(rk, (j + 2) * BC, kbuf(P), wave_u, lane);
+    if (HAS_NEXT) tile_to_lds<BC, true>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_NEXT) {
+      floatx16 s[2];
+      scores(kbuf(P ^ 1), s);
+      bf16x8 pn[4];
+      bool rs;
+      const float alpha = softmax(s, pn, Nk - (j + 1) * BC, mask_next_tag, rs);
+      accumulate(vbuf(P), pb);
+      if (rs) rescale_o(alpha);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[i] = pn[i];
+      wait_vmem();
+      __syncthreads();
+    } else {
+      accumulate(vbuf(P), pb);
+    }
+  };
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  // iterations 0 .. n_tiles-3 compute S of a full tile
+  int j = 0;
+  for (; j + 1 < n_tiles - 2; j += 2) {
+    iteration(j, P0{}, T{}, F{});
+    iteration(j + 1, P1{}, T{}, F{});
+  }
+  if (j < n_tiles - 2) {
+    iteration(j, P0{}, T{}, F{});
     ++j;
   }
-  if (n_tiles > n_full) {
-    if (j & 1)
-      tile_step(j, std::true_type{}, S1{});
-    else
-      tile_step(j, std::true_type{}, S0{});
+  // iteration n_tiles-2 computes S of the last tile (masked if partial)
+  if (j == n_tiles - 2) {
+    if (j & 1) {
+      if (tail) iteration(j, P1{}, T{}, T{}); else iteration(j, P1{}, T{}, F{});
+    } else {
+      if (tail) iteration(j, P0{}, T{}, T{}); else iteration(j, P0{}, T{}, F{});
+    }
+    ++j;
   }
+  // last iteration: P V of the last tile only
+  if (j & 1) iteration(j, P1{}, F{}, F{}); else iteration(j, P0{}, F{}, F{});
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
   const float l_tot = wave_sum_halves(l_run);
@@ -356,7 +406,7 @@ int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v2: BR=128 (4 waves x 32 rows), BC=64, 2-stage direct-to-LDS K/V, "
+  return "gfx950 fa_fwd v3: BR=128 (4 waves x 32 rows), BC=64, K one tile ahead of V, direct-to-LDS, "
          "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16";
 }
 
