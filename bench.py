@@ -33,10 +33,17 @@ import fa06_inputs as fi  # noqa: E402
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense BF16 matrix peak
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b2_h16_n8192"
-# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
-# for the current kernel on the default workload, scaled by the copy-kernel
-# calibration factor; None until measured for this kernel version.
-MEASURED_TRAFFIC_BYTES = None
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# (one run each) on the default workload, each scaled by what the same counter
+# reads for a plain copy kernel of known size (read x2.000, write x1.000).
+# Reported only while the library's build string is the one measured; any
+# other kernel build reports null.
+MEASURED_TRAFFIC = {
+    "kernel": "gfx950 fa_fwd v3: BR=128 (4 waves x 32 rows), BC=64, K one tile ahead of V, "
+              "direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16",
+    "workload": "b2_h16_n8192",
+    "bytes": 350.3e6,
+}
 
 
 def parse():
@@ -171,7 +178,9 @@ def main():
         "peak": MFMA_BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-        "traffic": MEASURED_TRAFFIC_BYTES,
+        "traffic": (MEASURED_TRAFFIC["bytes"]
+                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"]
+                        and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
     }
     out = {
