@@ -1,0 +1,104 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source (a dropped
+term, a wrong sign, a transposed operand, a wrong index or stride), builds the
+mutant in a temporary directory and checks that at least one pin -- brute
+force, closed form, library routine or a limit -- rejects it.  Every mutant
+keeps all memory accesses inside the input buffers for the shapes used here.
+"""
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.special
+
+import fa06_inputs as fi
+import oracle
+from tests import bruteforce
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
+
+MUTATIONS = {
+    "scale dropped": ("s[j] = sigma * dot;", "s[j] = dot;"),
+    "exp sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
+    "K transposed": ("widen_bf16(K[j * d + c])", "widen_bf16(K[c * Nk + j])"),
+    "LSE max term dropped": ("*lse = m + log(l);", "*lse = log(l);"),
+    "no normalisation": ("for (int64_t c = 0; c < dv; ++c) o[c] /= l;", ""),
+    "always head 0": ("const int64_t bh = flat / Nq;", "const int64_t bh = 0;"),
+    "Q ignores head": ("attend_one_row(Q + flat * d,", "attend_one_row(Q + (flat % Nq) * d,"),
+    "min instead of max": ("if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    "count instead of sum": ("        l += s[j];", "        l += 1.0;"),
+    "V row stride off by one": ("o[c] += s[j] * widen_bf16(V[j * dv + c]);",
+                                "o[c] += s[j] * widen_bf16(V[(j > 0 ? j - 1 : 0) * dv + c]);"),
+}
+
+
+def build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not unique"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+                    str(path), "-o", str(lib), "-lm"], check=True)
+    so = ctypes.CDLL(str(lib))
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    so.oracle_attn_fp64.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float, p, p]
+    so.oracle_attn_fp64.restype = ctypes.c_int
+
+    def attention(Q, K, V, scale):
+        B, H, Nq, d = Q.shape
+        Nk, dv = K.shape[2], V.shape[3]
+        Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+        O = np.empty((B, H, Nq, dv))
+        L = np.empty((B, H, Nq))
+        rc = so.oracle_attn_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, B, H, Nq, Nk, d, dv,
+                                 ctypes.c_float(scale), O.ctypes.data, L.ctypes.data)
+        assert rc == 0
+        return O, L
+    return attention
+
+
+def widen(bits):
+    return fi.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def pins_pass(attention):
+    """True when every pin accepts the implementation."""
+    ok = True
+    # brute force, several heads and batches, Nk != d
+    Q, K, V = fi.make_qkv(2, 3, 5, 7, 16, seed=2)
+    O, L = attention(Q, K, V, 0.25)
+    Ob, Lb = bruteforce.attention(Q, K, V, 0.25)
+    ok &= np.allclose(O, Ob, rtol=0, atol=1e-12) and np.allclose(L, Lb, rtol=0, atol=1e-12)
+    # library softmax / logsumexp on a larger head
+    Q, K, V = fi.make_qkv(1, 2, 24, 40, 32, seed=3)
+    sc = float(np.float32(1 / math.sqrt(32)))
+    O, L = attention(Q, K, V, sc)
+    S = np.float64(np.float32(sc)) * (widen(Q) @ np.swapaxes(widen(K), -1, -2))
+    ok &= np.allclose(O, scipy.special.softmax(S, axis=-1) @ widen(V), rtol=0, atol=1e-12)
+    ok &= np.allclose(L, scipy.special.logsumexp(S, axis=-1), rtol=0, atol=1e-12)
+    # hardmax limit: large logits must neither overflow nor mix
+    Q, K, V = fi.make_qkv(1, 1, 16, 32, 64, seed=4)
+    with np.errstate(all="ignore"):
+        O, L = attention(Q, K, V, 500.0)
+    dots = widen(Q)[0, 0] @ widen(K)[0, 0].T
+    srt = np.sort(dots, axis=1)
+    sel = (srt[:, -1] - srt[:, -2]) > 0.1
+    am = dots.argmax(axis=1)
+    ok &= bool(np.all(np.isfinite(O))) and np.allclose(O[0, 0][sel], widen(V)[0, 0][am[sel]], atol=1e-6)
+    return bool(ok)
+
+
+def test_unmutated_oracle_passes_the_pins():
+    assert pins_pass(oracle.attention)
+
+
+@pytest.mark.parametrize("name", list(MUTATIONS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTATIONS[name]
+    attention = build_mutant(tmp_path, name, old, new)
+    assert not pins_pass(attention), f"mutation {name!r} was not detected by any pin"
