@@ -7,9 +7,10 @@ share only the seeded inputs.
 
 The arithmetic lives in ``fa_oracle.c``: exact scaled-dot-product attention
 as defined in "FlashAttention'ı Anlamak Bölüm 1", section 0.2 "Notasyon"
-(score and output equations, mask/bias term zero), evaluated row by row in
-fp64 from the bf16 input bits.  Outputs: O in fp64 (never rounded to bf16) and
-the natural-log log-sum-exp of the scaled logits per query row.
+(score and output equations, with the optional mask/bias term as an fp32
+additive bias and/or a causal mask), evaluated row by row in fp64 from the
+bf16 input bits.  Outputs: O in fp64 (never rounded to bf16) and the
+natural-log log-sum-exp of the scaled (and biased) logits per query row.
 """
 from __future__ import annotations
 
@@ -55,6 +56,10 @@ def _lib():
         lib.oracle_attn_rows_fp64.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
                                               ctypes.c_float, _p, _i64, _p, _p]
         lib.oracle_attn_rows_fp64.restype = ctypes.c_int
+        lib.oracle_attn_masked_fp64.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                ctypes.c_float, ctypes.c_int, _p, _i64, _i64, _i64,
+                                                _p, _i64, _p, _p]
+        lib.oracle_attn_masked_fp64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib_handle = lib
@@ -100,6 +105,46 @@ def attention_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, ro
                                       rows.ctypes.data, n, O.ctypes.data, LSE.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_attn_rows_fp64 failed with code {rc}")
+    return O, LSE
+
+
+def attention_masked(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, causal: bool = False,
+                     bias: np.ndarray | None = None, rows: np.ndarray | None = None):
+    """Attention with the optional mask/bias term.
+
+    ``causal`` hides key j from query i when j > i + (Nk - Nq).  ``bias`` is an
+    fp32 array broadcastable to [B, H, Nq, Nk] with unit key stride (zero
+    strides broadcast over batch / heads / rows).  Rows that see no key give
+    O = 0 and LSE = -inf.  With ``rows`` (flat indices into [B*H*Nq]) the
+    results are [n, dv] and [n]; without, [B, H, Nq, dv] and [B, H, Nq].
+    """
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    bias_ptr, sb, sh, sq = None, 0, 0, 0
+    if bias is not None:
+        bias = np.asarray(bias, dtype=np.float32)
+        full = np.broadcast_to(bias, (B, H, Nq, Nk))
+        if full.strides[3] != 4:
+            bias = np.ascontiguousarray(bias)
+            full = np.broadcast_to(bias, (B, H, Nq, Nk))
+        sb, sh, sq = (st // 4 for st in full.strides[:3])
+        bias_ptr = full.ctypes.data
+    if rows is None:
+        n = B * H * Nq
+        O = np.empty((B, H, Nq, dv), dtype=np.float64)
+        LSE = np.empty((B, H, Nq), dtype=np.float64)
+        rows_ptr = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.shape[0]
+        O = np.empty((n, dv), dtype=np.float64)
+        LSE = np.empty((n,), dtype=np.float64)
+        rows_ptr = rows.ctypes.data
+    rc = _lib().oracle_attn_masked_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data,
+                                        B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
+                                        bias_ptr, sb, sh, sq, rows_ptr, n, O.ctypes.data, LSE.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_masked_fp64 failed with code {rc}")
     return O, LSE
 
 

@@ -22,11 +22,16 @@ def _widen(bits):
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def attention(Q, K, V, scale):
+def attention(Q, K, V, scale, causal=False, bias=None):
+    """Optional mask/bias term: ``causal`` drops key j for query i when
+    j > i + (Nk - Nq); ``bias`` (float32, broadcastable to [B, H, Nq, Nk]) is
+    added to the scaled logits, and a key whose bias is -inf is dropped.  A
+    row left with no key gives O = 0 and LSE = -inf."""
     B, H, Nq, d = Q.shape
     Nk = K.shape[2]
     dv = V.shape[3]
     q, k, v = _widen(Q).tolist(), _widen(K).tolist(), _widen(V).tolist()
+    bb = None if bias is None else np.broadcast_to(np.asarray(bias, np.float32), (B, H, Nq, Nk)).astype(np.float64)
     sigma = float(np.float32(scale))
     O = np.zeros((B, H, Nq, dv))
     LSE = np.zeros((B, H, Nq))
@@ -34,12 +39,21 @@ def attention(Q, K, V, scale):
         for h in range(H):
             for i in range(Nq):
                 qi = q[b][h][i]
-                w = []
+                keys, w = [], []
                 for j in range(Nk):
+                    if causal and j > i + (Nk - Nq):
+                        continue
+                    extra = 0.0 if bb is None else float(bb[b, h, i, j])
+                    if extra == -math.inf:
+                        continue
                     dot = math.fsum(qi[c] * k[b][h][j][c] for c in range(d))
-                    w.append(math.exp(sigma * dot))
+                    keys.append(j)
+                    w.append(math.exp(sigma * dot + extra))
+                if not keys:
+                    LSE[b, h, i] = -math.inf
+                    continue
                 l = math.fsum(w)
                 for c in range(dv):
-                    O[b, h, i, c] = math.fsum(w[j] * v[b][h][j][c] for j in range(Nk)) / l
+                    O[b, h, i, c] = math.fsum(wj * v[b][h][j][c] for wj, j in zip(w, keys)) / l
                 LSE[b, h, i] = math.log(l)
     return O, LSE

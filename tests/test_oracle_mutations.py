@@ -24,7 +24,7 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
 MUTATIONS = {
     "scale dropped": ("s[j] = sigma * dot;", "s[j] = dot;"),
     "exp sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
-    "K transposed": ("widen_bf16(K[j * d + c])", "widen_bf16(K[c * Nk + j])"),
+    "K transposed": ("widen_bf16(K[j * d + c])", "widen_bf16(K[c * n_vis + j])"),
     "LSE max term dropped": ("*lse = m + log(l);", "*lse = log(l);"),
     "no normalisation": ("for (int64_t c = 0; c < dv; ++c) o[c] /= l;", ""),
     "always head 0": ("const int64_t bh = flat / Nq;", "const int64_t bh = 0;"),
@@ -33,6 +33,14 @@ MUTATIONS = {
     "count instead of sum": ("        l += s[j];", "        l += 1.0;"),
     "V row stride off by one": ("o[c] += s[j] * widen_bf16(V[j * dv + c]);",
                                 "o[c] += s[j] * widen_bf16(V[(j > 0 ? j - 1 : 0) * dv + c]);"),
+}
+
+# Mistakes in the mask/bias term, caught by the masked pins.
+MASK_MUTATIONS = {
+    "causal diagonal off by one": ("n_vis = i + (Nk - Nq) + 1;", "n_vis = i + (Nk - Nq);"),
+    "causal diagonal not aligned to the last key": ("n_vis = i + (Nk - Nq) + 1;", "n_vis = i + 1;"),
+    "bias subtracted": ("if (bias_row) s[j] += (double)bias_row[j];", "if (bias_row) s[j] -= (double)bias_row[j];"),
+    "bias head stride ignored": ("(bh % H) * bias_sh", "0 * bias_sh"),
 }
 
 
@@ -48,6 +56,9 @@ def build_mutant(tmp_path, name, old, new):
     i64, p = ctypes.c_int64, ctypes.c_void_p
     so.oracle_attn_fp64.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float, p, p]
     so.oracle_attn_fp64.restype = ctypes.c_int
+    so.oracle_attn_masked_fp64.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                           ctypes.c_int, p, i64, i64, i64, p, i64, p, p]
+    so.oracle_attn_masked_fp64.restype = ctypes.c_int
 
     def attention(Q, K, V, scale):
         B, H, Nq, d = Q.shape
@@ -59,6 +70,19 @@ def build_mutant(tmp_path, name, old, new):
                                  ctypes.c_float(scale), O.ctypes.data, L.ctypes.data)
         assert rc == 0
         return O, L
+
+    def masked(Q, K, V, scale, causal, bias):
+        B, H, Nq, d = Q.shape
+        Nk, dv = K.shape[2], V.shape[3]
+        full = np.ascontiguousarray(np.broadcast_to(bias, (B, H, Nq, Nk)).astype(np.float32))
+        O = np.empty((B, H, Nq, dv))
+        L = np.empty((B, H, Nq))
+        rc = so.oracle_attn_masked_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, B, H, Nq, Nk, d, dv,
+                                        ctypes.c_float(scale), int(causal), full.ctypes.data,
+                                        H * Nq * Nk, Nq * Nk, Nk, None, B * H * Nq, O.ctypes.data, L.ctypes.data)
+        assert rc == 0
+        return O, L
+    attention.masked = masked
     return attention
 
 
@@ -102,3 +126,30 @@ def test_mutant_is_caught(tmp_path, name):
     old, new = MUTATIONS[name]
     attention = build_mutant(tmp_path, name, old, new)
     assert not pins_pass(attention), f"mutation {name!r} was not detected by any pin"
+
+
+def masked_pins_pass(masked):
+    """Brute force with a causal mask (Nq < Nk and Nq > Nk) and a per-head bias."""
+    ok = True
+    rng = np.random.default_rng(5)
+    for Nq, Nk in ((4, 9), (9, 4)):
+        Q, K, V = fi.make_qkv(1, 2, Nq, Nk, 16, seed=6)
+        bias = rng.standard_normal((1, 2, Nq, Nk)).astype(np.float32)
+        O, L = masked(Q, K, V, 0.3, True, bias)
+        Ob, Lb = bruteforce.attention(Q, K, V, 0.3, causal=True, bias=bias)
+        fin = np.isfinite(Lb)
+        ok &= np.allclose(O, Ob, rtol=0, atol=1e-12) and np.array_equal(np.isfinite(L), fin)
+        ok &= np.allclose(L[fin], Lb[fin], rtol=0, atol=1e-12)
+    return bool(ok)
+
+
+@pytest.mark.parametrize("name", list(MASK_MUTATIONS))
+def test_mask_mutant_is_caught(tmp_path, name):
+    old, new = MASK_MUTATIONS[name]
+    attention = build_mutant(tmp_path, name, old, new)
+    assert not masked_pins_pass(attention.masked), f"mutation {name!r} was not detected by any pin"
+
+
+def test_unmutated_oracle_passes_the_masked_pins(tmp_path):
+    attention = build_mutant(tmp_path, "none", "int oracle_max_threads(void)", "int oracle_max_threads(void)")
+    assert masked_pins_pass(attention.masked)
