@@ -54,6 +54,9 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=fi.WORKLOAD_ORDER)
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the oracle sample (CPU baseline)")
+    p.add_argument("--causal", action="store_true",
+                   help="causal mask (key j hidden from query i when j > i + Nk - Nq); throughput counts "
+                        "only the visible (query, key) pairs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of attention, run a plain copy kernel (256 MiB read + 256 MiB "
@@ -83,7 +86,16 @@ def calibrate_copy(args):
                       "GB_per_s": round(8 * n / ms / 1e6, 1), "steps": args.steps}), flush=True)
 
 
-def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None):
+def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
+    """(query, key) pairs one head computes: Nq*Nk, or the causal count."""
+    if not causal:
+        return Nq * Nk
+    off = Nk - Nq
+    i = np.arange(Nq, dtype=np.int64)
+    return int(np.clip(i + off + 1, 0, Nk).sum())
+
+
+def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
     import oracle
     import torch
     per_row_flop = 4 * w.Nk * w.d
@@ -92,20 +104,33 @@ def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None):
     # calibrate on a small sample, then size the timed sample to ~target_s
     n0 = 64
     rows0 = np.sort(rng.choice(total_rows, size=n0, replace=False)).astype(np.int64)
+
+    def run(rows):
+        if causal:
+            return oracle.attention_masked(Q, K, V, w.scale, causal=True, rows=rows)
+        return oracle.attention_rows(Q, K, V, w.scale, rows)
+
+    def flops(rows):
+        if not causal:
+            return len(rows) * per_row_flop
+        i = rows % w.Nq
+        return int(np.clip(i + (w.Nk - w.Nq) + 1, 0, w.Nk).sum()) * 4 * w.d
+
     t0 = time.perf_counter()
-    oracle.attention_rows(Q, K, V, w.scale, rows0)
+    run(rows0)
     dt0 = time.perf_counter() - t0
     n = int(min(total_rows, max(n0, n0 * target_s / max(dt0, 1e-6))))
     rows = np.sort(rng.choice(total_rows, size=n, replace=False)).astype(np.int64)
     t0 = time.perf_counter()
-    Oo, Lo = oracle.attention_rows(Q, K, V, w.scale, rows)
+    Oo, Lo = run(rows)
     dt = time.perf_counter() - t0
     res = {
-        "value": n * per_row_flop / dt / 1e12,
+        "value": flops(rows) / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.max_threads(),
         "kind": "oracle",
-        "sample": f"{n} of {total_rows} query rows of {w.name} (all {w.Nk} keys each), fp64, {dt:.1f} s",
+        "sample": f"{n} of {total_rows} query rows of {w.name}{' causal' if causal else ''} "
+                  f"(all their visible keys), fp64, {dt:.1f} s",
     }
     parity = None
     if o_gpu is not None:
@@ -145,11 +170,18 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     lib = fa.load_library()
-    call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-                 w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
+    if args.causal:
+        call = fa.fa_fwd_masked_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.scale, 1, None, 0, 0, 0, sptr)
+    else:
+        call = fa.fa_fwd_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
+    flop = 4 * w.B * w.H * w.d * visible_pairs(w.Nq, w.Nk, args.causal)
 
     def step():
-        rc = fa.fa_fwd_raw(*call_args)
+        rc = call(*call_args)
         if rc != 0:
             raise fa.FaError(rc, fa.fa_status_string(rc))
 
@@ -170,8 +202,8 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
     ms_per_step = wall * 1e3 / args.steps
-    value = w.flops / (ms_per_step * 1e-3) / 1e12
-    achieved = w.flops / (ev_ms * 1e-3) / 1e12
+    value = flop / (ms_per_step * 1e-3) / 1e12
+    achieved = flop / (ev_ms * 1e-3) / 1e12
     roof = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
@@ -179,7 +211,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "traffic": (MEASURED_TRAFFIC["bytes"]
-                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"]
+                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal
                         and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
     }
@@ -196,15 +228,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": False, "scale": w.scale, "seed": w.seed,
+        "config": {"workload": w.name + ("+causal" if args.causal else ""), "B": w.B, "H": w.H,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": bool(args.causal), "flop_per_step": flop, "scale": w.scale, "seed": w.seed,
                    "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
                    "kernel": fa.fa_build_info()},
         "roofline": roof,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse)
+        cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse, causal=args.causal)
         out["cpu_baseline"] = cb
         out["parity_sampled"] = parity
     print(json.dumps(out), flush=True)

@@ -58,6 +58,9 @@ def load_library(path: str | None = None):
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float, vp]
     lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                  ctypes.c_int, vp, i64, i64, i64, vp]
+    lib.fa_fwd_masked.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_build_info.argtypes = []
@@ -82,14 +85,24 @@ def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
                                  ctypes.c_float(scale), stream)
 
 
-def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None):
+def fa_fwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                      B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int,
+                      bias_ptr: int | None, sb: int, sh: int, sq: int, stream: int) -> int:
+    """Direct call of the C ``fa_fwd_masked``; returns the status."""
+    return load_library().fa_fwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d,
+                                        ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq, stream)
+
+
+def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False):
     """Fused attention forward on torch tensors.
 
     q: [B, H, Nq, 128] bf16, k and v: [B, H, Nk, 128] bf16, all contiguous on
-    the same HIP device.  ``scale`` defaults to 1/sqrt(128).  Returns
-    ``(o, lse)``: o [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional
-    ``out`` / ``lse`` tensors of those shapes receive the results.  The call
-    is enqueued on the current stream of q's device.
+    the same HIP device.  ``scale`` defaults to 1/sqrt(128).  With
+    ``causal``, key j is hidden from query i when j > i + (Nk - Nq) (rows that
+    see no key give O = 0, LSE = -inf).  Returns ``(o, lse)``: o
+    [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional ``out`` / ``lse``
+    tensors of those shapes receive the results.  The call is enqueued on the
+    current stream of q's device.
     """
     import torch
 
@@ -124,12 +137,16 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None):
         raise ValueError("lse must be a contiguous fp32 tensor [B, H, Nq] on q's device")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        rc = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                        B, H, Nq, Nk, d, float(scale), stream)
+        if causal:
+            rc = fa_fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   B, H, Nq, Nk, d, float(scale), 1, None, 0, 0, 0, stream)
+        else:
+            rc = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, Nq, Nk, d, float(scale), stream)
     if rc != 0:
         raise FaError(rc, fa_status_string(rc))
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+__all__ = ["fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS"]

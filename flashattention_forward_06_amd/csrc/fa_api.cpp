@@ -40,20 +40,24 @@ int check_device() {
 
 }  // namespace
 
-extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                      float scale, void* stream) {
+namespace {
+
+int validate_and_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
+                        int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
+                        void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
   if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (bias != nullptr) return FA_ERR_UNSUPPORTED;  // additive bias: not in this build
   // sizes: B*H*N*d*2 bytes must fit in int64 (N <= 2^23, d*2 = 2^8)
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
   const int64_t row_bytes = FA_HEAD_DIM * 2;
   if (BH > (INT64_MAX / row_bytes) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
-  // one workgroup per 128 query rows of a head; the grid has < 2^31 workgroups
   // a pointer may be NULL only when its buffer is empty
   if ((BH * Nq > 0 && (!Q || !O || !LSE)) || (BH > 0 && (!K || !V))) return FA_ERR_NULL_POINTER;
+  // one workgroup per 128 query rows of a head; the grid has < 2^31 workgroups
   if (BH * ((Nq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_INVALID_SCALE;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
@@ -66,9 +70,27 @@ extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, floa
   if (BH * Nq == 0) return FA_OK;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
-  if (fa06::launch_fa_fwd(Q, K, V, O, LSE, BH, Nq, Nk, scale, static_cast<hipStream_t>(stream)) != 0)
+  if (fa06::launch_fa_fwd(Q, K, V, O, LSE, BH, Nq, Nk, scale, causal == 1, static_cast<hipStream_t>(stream)) != 0)
     return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                      int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                      float scale, void* stream) {
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, 0, nullptr, stream);
+}
+
+extern "C" int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
+                             int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                             int causal, const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                             int64_t bias_stride_q, void* stream) {
+  (void)bias_stride_b;
+  (void)bias_stride_h;
+  (void)bias_stride_q;
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, bias, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {

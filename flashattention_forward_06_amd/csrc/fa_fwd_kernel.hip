@@ -43,6 +43,10 @@
 //   * Workgroup ids are remapped so the q-tiles of one head run on the same
 //     XCD (workgroups are dispatched round-robin over the 8 XCDs), sharing
 //     that head's K/V in the XCD's L2.
+//   * Causal variant (the mask term of the score equation): a q-tile stops
+//     at the last K/V tile its last row can see, only tiles that cross the
+//     diagonal are masked per key, and the q-tiles with the most work are
+//     dispatched first.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -129,10 +133,16 @@ __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char
   }
 }
 
+// Every helper lambda of the kernel is inlined: the loop body must stay one
+// straight-line region with all state in registers.
+#define FA_INLINE __attribute__((always_inline))
+
 // Wait until this wave's outstanding global loads (incl. LDS-direct) landed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-template <bool NEG_SCALE>
+// CAUSAL: key j is hidden from query i when j > i + (Nk - Nq); tiles past a
+// q-tile's diagonal are skipped, tiles crossing it are masked per element.
+template <bool NEG_SCALE, bool CAUSAL>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -152,7 +162,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int nfull = nblk & ~7;
   if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
   const int bh = bid / n_qtiles;
-  const int qt = bid - bh * n_qtiles;
+  int qt = bid - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
 
   const size_t head_q = (size_t)bh * (size_t)Nq * D;
@@ -163,17 +174,41 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * ROW_BYTES);
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int n_full = Nk / BC;                 // tiles with BC valid keys
-  const int n_tiles = n_full + (Nk % BC != 0);
-  const bool tail = n_tiles > n_full;
+  const int n_full = Nk / BC;  // tiles with BC valid keys
+  int n_tiles = n_full + (Nk % BC != 0);
+  int first_masked = n_full;   // first tile that needs per-key masks
+  // last key visible to this lane's query row (keys above it are masked)
+  int key_lim = Nk - 1;
+  if constexpr (CAUSAL) {
+    const int off = Nk - Nq;
+    const int q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;
+    const int lim_last = q_last + off;  // the q-tile's last row sees keys <= lim_last
+    const int lim_first = q0 + off;     // its first row sees keys <= lim_first
+    const int need = lim_last < 0 ? 0 : lim_last / BC + 1;
+    n_tiles = need < n_tiles ? need : n_tiles;
+    const int unmasked = lim_first + 1 <= 0 ? 0 : (lim_first + 1) / BC;
+    first_masked = unmasked < first_masked ? unmasked : first_masked;
+    const int my_lim = q0 + wave * 32 + c + off;
+    key_lim = my_lim < key_lim ? my_lim : key_lim;
+    if (n_tiles == 0) {
+      // no row of this q-tile sees any key: O = 0, LSE = -inf
+      const int q = q0 + wave * 32 + c;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)  // this lane's half row: bytes [128h, 128h + 128)
+        __builtin_amdgcn_raw_buffer_store_b128(uintx4{0u, 0u, 0u, 0u}, ro,
+                                               (uint32_t)q * ROW_BYTES + 128u * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
+      if (h == 0 && q < Nq) LSE[(size_t)bh * Nq + q] = -__builtin_inff();
+      return;
+    }
+  }
 
   // LDS: K buffers at [0, 32K), V buffers at [32K, 64K).  K runs one tile
   // ahead of V: while tile j's P V is accumulated, tile j+1's scores are
   // computed, so K(j+1) and V(j) are resident together.
   char* const kbuf0 = smem;
   char* const vbuf0 = smem + 2 * TILE_BYTES;
-  auto kbuf = [&](int i) { return kbuf0 + i * TILE_BYTES; };
-  auto vbuf = [&](int i) { return vbuf0 + i * TILE_BYTES; };
+  auto kbuf = [&](int i) FA_INLINE { return kbuf0 + i * TILE_BYTES; };
+  auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * TILE_BYTES; };
 
   // ---- prologue: Q (staged in the V buffers), K(0), K(1).
   tile_to_lds<BR, false>(rq, q0, vbuf0, wave_u, lane);
@@ -199,7 +234,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
   // S^T = K Q^T for the 64 keys of one K buffer (two 32-key blocks).
-  auto scores = [&](const char* ks, floatx16 (&s)[2]) {
+  auto scores = [&](const char* ks, floatx16 (&s)[2]) FA_INLINE {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = floatx16{};
@@ -216,7 +251,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // product).  Branch free: the decision to raise the running max is wave
   // uniform (ballot); returns the factor the output accumulator must be
   // multiplied by before this tile's P V is added (1 when unchanged).
-  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pb)[4], int valid, auto mask_tag, bool& rescale) -> float {
+  // MASK tiles hide the keys above `lim` (this row's last visible key,
+  // relative to the tile's first key).
+  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pb)[4], int lim, auto mask_tag, bool& rescale) FA_INLINE -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
     if constexpr (MASK) {
 #pragma unroll
@@ -224,7 +261,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= valid) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
+          if (key > lim) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
         }
     }
     float ext = s[0][0];
@@ -236,7 +273,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const float m_tile = ext * c_log2;
     rescale = __ballot(m_tile > m_run + RESCALE_SLACK) != 0;
     const float m_new = rescale ? fmaxf(m_run, m_tile) : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    // a causal row that has seen no key yet keeps m = -inf (and l = 0)
+    if constexpr (CAUSAL) alpha = m_new == -__builtin_inff() ? 1.0f : alpha;
     m_run = m_new;
     float lsum = 0.0f;
 #pragma unroll
@@ -246,7 +285,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
         if constexpr (MASK) {
           const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= valid) p = 0.0f;
+          if (key > lim) p = 0.0f;
         }
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
@@ -256,7 +295,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // O^T += V^T P^T for the 64 keys of one V buffer: 4 d-blocks x 4 key steps.
-  auto accumulate = [&](const char* vs, const bf16x8 (&pb)[4]) {
+  auto accumulate = [&](const char* vs, const bf16x8 (&pb)[4]) FA_INLINE {
     const int g = lane >> 4;          // 16-lane group
     const int i16 = lane & 15;
     const int sub = i16 >> 2;         // which of the 4 keys this lane addresses
@@ -285,7 +324,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  auto rescale_o = [&](float alpha) {
+  auto rescale_o = [&](float alpha) FA_INLINE {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -298,12 +337,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     floatx16 s[2];
     scores(kbuf(0), s);
     bool rs;
-    float alpha;
-    if (n_tiles == 1 && tail)
-      alpha = softmax(s, pb, Nk, std::true_type{}, rs);
+    if (first_masked == 0)
+      softmax(s, pb, key_lim, std::true_type{}, rs);
     else
-      alpha = softmax(s, pb, Nk, std::false_type{}, rs);
-    (void)alpha;  // O is still zero
+      softmax(s, pb, key_lim, std::false_type{}, rs);
+    // O is still zero: no rescale needed
   }
   wait_vmem();
   __syncthreads();
@@ -313,7 +351,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // the iteration prefetches K(j+2) into kbuf(j&1) and V(j+1) into
   // vbuf((j+1)&1), whose previous contents were consumed before the last
   // barrier.
-  auto iteration = [&](int j, auto par_tag, auto has_next_tag, auto mask_next_tag) {
+  auto iteration = [&](int j, auto par_tag, auto has_next_tag, auto mask_next_tag) FA_INLINE {
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
     if (j + 2 < n_tiles) tile_to_lds<BC, false>(rk, (j + 2) * BC, kbuf(P), wave_u, lane);
@@ -323,7 +361,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       scores(kbuf(P ^ 1), s);
       bf16x8 pn[4];
       bool rs;
-      const float alpha = softmax(s, pn, Nk - (j + 1) * BC, mask_next_tag, rs);
+      const float alpha = softmax(s, pn, key_lim - (j + 1) * BC, mask_next_tag, rs);
       accumulate(vbuf(P), pb);
       if (rs) rescale_o(alpha);
 #pragma unroll
@@ -339,31 +377,56 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using P1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
-  // iterations 0 .. n_tiles-3 compute S of a full tile
-  int j = 0;
-  for (; j + 1 < n_tiles - 2; j += 2) {
-    iteration(j, P0{}, T{}, F{});
-    iteration(j + 1, P1{}, T{}, F{});
-  }
-  if (j < n_tiles - 2) {
-    iteration(j, P0{}, T{}, F{});
-    ++j;
-  }
-  // iteration n_tiles-2 computes S of the last tile (masked if partial)
-  if (j == n_tiles - 2) {
-    if (j & 1) {
-      if (tail) iteration(j, P1{}, T{}, T{}); else iteration(j, P1{}, T{}, F{});
-    } else {
-      if (tail) iteration(j, P0{}, T{}, T{}); else iteration(j, P0{}, T{}, F{});
+  if constexpr (!CAUSAL) {
+    // iterations 0 .. n_tiles-3 compute S of a full tile
+    int j = 0;
+    for (; j + 1 < n_tiles - 2; j += 2) {
+      iteration(j, P0{}, T{}, F{});
+      iteration(j + 1, P1{}, T{}, F{});
     }
-    ++j;
+    if (j < n_tiles - 2) {
+      iteration(j, P0{}, T{}, F{});
+      ++j;
+    }
+    // iteration n_tiles-2 computes S of the last tile (masked if partial)
+    if (j == n_tiles - 2) {
+      const bool tail = first_masked < n_tiles;
+      if (j & 1) {
+        if (tail) iteration(j, P1{}, T{}, T{}); else iteration(j, P1{}, T{}, F{});
+      } else {
+        if (tail) iteration(j, P0{}, T{}, T{}); else iteration(j, P0{}, T{}, F{});
+      }
+    }
+  } else {
+    // Iterations j in [j0, j1) all compute S of a next tile with the same
+    // masking; the K/V buffer parity (j & 1) is a compile-time constant of
+    // each instantiation, so the loop is unrolled by two.
+    auto run = [&](int j0, int j1, auto mask_tag) FA_INLINE {
+      int j = j0;
+      if (j < j1 && (j & 1)) {
+        iteration(j, P1{}, T{}, mask_tag);
+        ++j;
+      }
+      for (; j + 1 < j1; j += 2) {
+        iteration(j, P0{}, T{}, mask_tag);
+        iteration(j + 1, P1{}, T{}, mask_tag);
+      }
+      if (j < j1) iteration(j, P0{}, T{}, mask_tag);
+    };
+    // the next tile is unmasked for j + 1 < first_masked, masked from there on
+    // (only the few tiles that cross the diagonal or hold the Nk tail)
+    int j_split = first_masked - 1;
+    j_split = j_split < 0 ? 0 : (j_split > n_tiles - 1 ? n_tiles - 1 : j_split);
+    run(0, j_split, F{});
+    run(j_split, n_tiles - 1, T{});
   }
   // last iteration: P V of the last tile only
-  if (j & 1) iteration(j, P1{}, F{}, F{}); else iteration(j, P0{}, F{}, F{});
+  if ((n_tiles - 1) & 1) iteration(n_tiles - 1, P1{}, F{}, F{}); else iteration(n_tiles - 1, P0{}, F{}, F{});
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
   const float l_tot = wave_sum_halves(l_run);
-  const float inv_l = 1.0f / l_tot;
+  // l = 0 only for a causal row that sees no key: O = 0, LSE = -inf
+  const float inv_l = (CAUSAL && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
   const int q = q0 + wave * 32 + c;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
@@ -383,14 +446,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   if (h == 0 && q < Nq) {
     const float ln2 = 0.69314718055994530942f;
-    LSE[(size_t)bh * Nq + q] = (m_run + __log2f(l_tot)) * ln2;
+    LSE[(size_t)bh * Nq + q] = (CAUSAL && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * ln2;
   }
 }
 
 }  // namespace
 
 int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                  int64_t BH, int64_t Nq, int64_t Nk, float scale, hipStream_t stream) {
+                  int64_t BH, int64_t Nq, int64_t Nk, float scale, bool causal, hipStream_t stream) {
   const int n_qtiles = (int)((Nq + BR - 1) / BR);
   const int64_t nblk = BH * n_qtiles;
   const float c_log2 = (float)((double)scale * 1.4426950408889634074);
@@ -400,14 +463,16 @@ int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L
   uint16_t* o = static_cast<uint16_t*>(O);
   int nq = (int)Nq, nk = (int)Nk;
   void* args[] = {&q, &k, &v, &o, &LSE, &nq, &nk, (void*)&n_qtiles, (void*)&c_log2};
-  const void* fn = scale < 0.0f ? (const void*)&fa_fwd_kernel<true> : (const void*)&fa_fwd_kernel<false>;
+  const bool neg = scale < 0.0f;
+  const void* fn = causal ? (neg ? (const void*)&fa_fwd_kernel<true, true> : (const void*)&fa_fwd_kernel<false, true>)
+                          : (neg ? (const void*)&fa_fwd_kernel<true, false> : (const void*)&fa_fwd_kernel<false, false>);
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v3: BR=128 (4 waves x 32 rows), BC=64, K one tile ahead of V, direct-to-LDS, "
-         "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16";
+  return "gfx950 fa_fwd v3.1: BR=128 (4 waves x 32 rows), BC=64, K one tile ahead of V, direct-to-LDS, "
+         "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16; causal variant with tile skipping";
 }
 
 }  // namespace fa06

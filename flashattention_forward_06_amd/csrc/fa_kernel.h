@@ -4,9 +4,10 @@
 #include <stdint.h>
 
 namespace fa06 {
-// Enqueue the forward kernel for BH = B*H independent heads.  Arguments are
-// already validated by the caller.  Returns 0 or the hipError_t of the launch.
+// Enqueue the forward kernel for BH = B*H independent heads (causal: key j
+// hidden from query i when j > i + Nk - Nq).  Arguments are already validated
+// by the caller.  Returns 0 or the hipError_t of the launch.
 int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                  int64_t BH, int64_t Nq, int64_t Nk, float scale, hipStream_t stream);
+                  int64_t BH, int64_t Nq, int64_t Nk, float scale, bool causal, hipStream_t stream);
 const char* kernel_config_string();
 }  // namespace fa06

@@ -87,6 +87,29 @@ int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
            float scale, void *stream);
 
+/*
+ * fa_fwd_masked -- fa_fwd with the optional mask/bias term of the score
+ * equation ("FlashAttention'ı Anlamak Bölüm 1", section 0.2: S = Q K^T / sqrt(d)
+ * + B).
+ *
+ *   causal   0 or 1.  With 1, key j is hidden from query i when
+ *            j > i + (Nk - Nq): the diagonal is aligned to the last query and
+ *            the last key (for Nq = Nk, row i sees keys 0..i).  Key tiles that
+ *            lie entirely past a query tile's diagonal are skipped.  A row that
+ *            sees no key (only when Nq > Nk) gets O = 0 and LSE = -inf.
+ *   bias     additive fp32 bias, added to scale * q_i . k_j in natural-log
+ *            units; element (b, h, i, j) is bias[b*bias_stride_b +
+ *            h*bias_stride_h + i*bias_stride_q + j].  Must be NULL in this
+ *            build (a non-NULL bias returns FA_ERR_UNSUPPORTED); the strides
+ *            are then ignored.
+ *   other arguments, ownership, execution and errors as for fa_fwd; a causal
+ *   value other than 0 or 1 returns FA_ERR_UNSUPPORTED.
+ */
+int fa_fwd_masked(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                  int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                  int64_t bias_stride_q, void *stream);
+
 /* fa_status_string -- static, NUL-terminated description of a status code. */
 const char *fa_status_string(int status);
 

@@ -21,7 +21,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_fwd", "fa_status_string"]
+    assert names == ["fa_build_info", "fa_fwd", "fa_fwd_masked", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
 
@@ -56,6 +56,22 @@ def call(q=Qp, k=Kp, v=Vp, o=Op, lse=Lp, **kw):
 ])
 def test_validation_codes(kw, code):
     assert call(**kw) == code
+
+
+def call_masked(causal=1, bias=None, **kw):
+    a = {**GOOD, **kw}
+    return fa.fa_fwd_masked_raw(Qp, Kp, Vp, Op, Lp, a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
+                                causal, bias, 0, 0, 0, 0)
+
+
+def test_masked_entry_validation():
+    assert call_masked(causal=2) == 3
+    assert call_masked(causal=-1) == 3
+    assert call_masked(bias=0x60000000) == 3      # additive bias is not in this build
+    assert call_masked(Nk=0) == 2
+    assert call_masked(d=64) == 3
+    assert call_masked(scale=float("nan")) == 5
+    assert call_masked(Nq=0) == 0
 
 
 def test_empty_problem_is_noop():

@@ -153,3 +153,57 @@ def test_single_hip_runtime(fa):
     paths = {ln.split()[-1] for ln in maps if "libamdhip64" in ln}
     assert len(paths) == 1, paths
     assert any("libfa06.so" in ln for ln in maps)
+
+
+CAUSAL_CASES = [
+    # B, H, Nq, Nk, seed, note
+    (1, 2, 256, 256, 80, "square, tile aligned"),
+    (2, 1, 200, 333, 81, "Nk > Nq, ragged"),
+    (1, 2, 300, 130, 82, "Nq > Nk: leading rows see no key"),
+    (1, 1, 1, 1, 83, "single query and key"),
+    (1, 1, 129, 65, 84, "one row past a q tile, one key past a kv tile"),
+    (1, 1, 640, 640, 85, "several q tiles, diagonal through every one"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,note", CAUSAL_CASES)
+def test_causal_full_compare(fa, B, H, Nq, Nk, seed, note):
+    import torch
+    say(f"case causal B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(128), causal=True)
+    torch.cuda.synchronize()
+    Og, Lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    Oo, Lo = oracle.attention_masked(Q, K, V, 1 / math.sqrt(128), causal=True)
+    none = np.isneginf(Lo)
+    assert np.array_equal(np.isneginf(Lg), none), "rows that see no key must report LSE = -inf"
+    assert np.all(Og[none] == 0)
+    check_parity(Og[~none], Lg[~none], Oo[~none], Lo[~none], f"causal {note}")
+
+
+def test_causal_offset_keys_sampled(fa):
+    import torch
+    say("case causal koffset: K*4, 1% rows +8, B=1 H=4 N=4096")
+    Q, K, V = fi.make_qkv(1, 4, 4096, 4096, 128, seed=86, k_scale=4.0, offset_frac=0.01, offset=8.0)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(128), causal=True)
+    torch.cuda.synchronize()
+    rows = fi.sample_rows(1, 4, 4096, 192, seed=86)
+    Or, Lr = oracle.attention_masked(Q, K, V, 1 / math.sqrt(128), causal=True, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    check_parity(o.view(-1, 128)[idx].float().cpu().numpy().astype(np.float64),
+                 lse.view(-1)[idx].cpu().numpy().astype(np.float64), Or, Lr, "causal koffset (sampled)")
+
+
+def test_noncausal_unchanged_by_masked_entry(fa):
+    import torch
+    Q, K, V = fi.make_qkv(1, 2, 200, 300, 128, seed=87)
+    q, k, v = to_dev(Q), to_dev(K), to_dev(V)
+    o1, l1 = fa.fa_fwd(q, k, v)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    rc = fa.fa_fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(),
+                              1, 2, 200, 300, 128, 1 / math.sqrt(128), 0, None, 0, 0, 0,
+                              torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
