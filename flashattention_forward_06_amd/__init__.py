@@ -1,9 +1,10 @@
 """MI355X (gfx950) fused attention forward: Python binding of ``libfa06.so``.
 
-``fa_fwd(q, k, v, scale=None) -> (o, lse)`` computes exact, dense, non-causal
-scaled-dot-product attention, ``O = softmax_row(scale * Q K^T) V``, plus the
-natural-log log-sum-exp of each row ("FlashAttention'ı Anlamak Bölüm 1",
-section 0.2, score and output equations without the mask term).  Tensors
+``fa_fwd(q, k, v, scale=None) -> (o, lse)`` computes exact, dense
+scaled-dot-product attention, ``O = softmax_row(scale * Q K^T + B) V``, plus
+the natural-log log-sum-exp of each row ("FlashAttention'ı Anlamak Bölüm 1",
+section 0.2, score and output equations), where the optional mask/bias term
+B is a causal mask and/or an fp32 additive bias.  Tensors
 are BF16 ``[B, H, N, 128]`` on an MI355X; the work runs in the HIP kernel of
 ``libfa06.so``.  This module only marshals arguments: PyTorch provides device
 memory and the current stream.  There is no fallback: if the library is
@@ -93,16 +94,50 @@ def fa_fwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: i
                                         ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq, stream)
 
 
-def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False):
+def _bias_arg(bias, B: int, H: int, Nq: int, Nk: int, device):
+    """Bias tensor -> (tensor kept alive, element strides) in the layout the
+    library reads: unit key stride and row/head/batch strides that are
+    multiples of 4 elements, from a 16-byte aligned base.  Broadcast
+    dimensions keep stride 0; anything else is copied once into a padded
+    buffer of that layout (argument marshalling, no arithmetic)."""
+    import torch
+
+    if not isinstance(bias, torch.Tensor):
+        raise TypeError("bias must be a torch.Tensor")
+    if bias.dtype != torch.float32:
+        raise TypeError(f"bias must be float32, got {bias.dtype}")
+    if bias.device != device:
+        raise ValueError("bias must be on q's device")
+    try:
+        full = bias.expand(B, H, Nq, Nk)
+    except RuntimeError as e:
+        raise ValueError(f"bias of shape {tuple(bias.shape)} does not broadcast to {(B, H, Nq, Nk)}") from e
+    st = full.stride()
+    ok = (Nk == 1 or st[3] == 1) and all(x >= 0 and x % 4 == 0 for x in st[:3]) and full.data_ptr() % 16 == 0
+    if ok:
+        return full, st[0], st[1], st[2]
+    # copy into [b', h', q', ceil4(Nk)] keeping broadcast dimensions at size 1
+    red = [1 if st[i] == 0 else n for i, n in enumerate((B, H, Nq))]
+    nk4 = (Nk + 3) // 4 * 4
+    buf = torch.zeros(red + [nk4], dtype=torch.float32, device=device)
+    buf[..., :Nk].copy_(full[:red[0], :red[1], :red[2]])
+    full = buf[..., :Nk].expand(B, H, Nq, Nk)
+    st = full.stride()
+    return full, st[0], st[1], st[2]
+
+
+def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False, bias=None):
     """Fused attention forward on torch tensors.
 
     q: [B, H, Nq, 128] bf16, k and v: [B, H, Nk, 128] bf16, all contiguous on
     the same HIP device.  ``scale`` defaults to 1/sqrt(128).  With
-    ``causal``, key j is hidden from query i when j > i + (Nk - Nq) (rows that
-    see no key give O = 0, LSE = -inf).  Returns ``(o, lse)``: o
-    [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional ``out`` / ``lse``
-    tensors of those shapes receive the results.  The call is enqueued on the
-    current stream of q's device.
+    ``causal``, key j is hidden from query i when j > i + (Nk - Nq).
+    ``bias`` (optional) is an fp32 tensor broadcastable to [B, H, Nq, Nk],
+    added to the scaled scores.  Rows that see no key (causal with Nq > Nk,
+    or a bias of -inf on every key) give O = 0, LSE = -inf.  Returns
+    ``(o, lse)``: o [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional
+    ``out`` / ``lse`` tensors of those shapes receive the results.  The call is
+    enqueued on the current stream of q's device.
     """
     import torch
 
@@ -135,11 +170,15 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
             or lse.device != q.device:
         raise ValueError("lse must be a contiguous fp32 tensor [B, H, Nq] on q's device")
+    bias_t, sb, sh, sq = None, 0, 0, 0
+    if bias is not None:
+        bias_t, sb, sh, sq = _bias_arg(bias, B, H, Nq, Nk, q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        if causal:
+        if causal or bias_t is not None:
             rc = fa_fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                   B, H, Nq, Nk, d, float(scale), 1, None, 0, 0, 0, stream)
+                                   B, H, Nq, Nk, d, float(scale), int(bool(causal)),
+                                   None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, stream)
         else:
             rc = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                             B, H, Nq, Nk, d, float(scale), stream)

@@ -42,19 +42,36 @@ int check_device() {
 
 namespace {
 
+// Largest per-wave bias extent, in elements: 31 row strides + one row + a
+// tile of slack must stay below 2^29 so every byte offset fits 31 bits.
+constexpr int64_t kBiasWaveSpan = int64_t(1) << 29;
+// Largest bias extent over all (b, h, i, j), in elements.
+constexpr int64_t kBiasMaxExtent = int64_t(1) << 60;
+
 int validate_and_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
                         int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
-                        void* stream) {
+                        int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
   if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
-  if (bias != nullptr) return FA_ERR_UNSUPPORTED;  // additive bias: not in this build
   // sizes: B*H*N*d*2 bytes must fit in int64 (N <= 2^23, d*2 = 2^8)
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
   const int64_t row_bytes = FA_HEAD_DIM * 2;
   if (BH > (INT64_MAX / row_bytes) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
+  // bias: non-negative element strides; the extent must be addressable
+  int64_t bias_elems = 0;
+  if (bias != nullptr) {
+    if (bias_sb < 0 || bias_sh < 0 || bias_sq < 0) return FA_ERR_UNSUPPORTED;
+    if (BH * Nq > 0) {
+      const __int128 ext = (__int128)(B - 1) * bias_sb + (__int128)(H - 1) * bias_sh +
+                           (__int128)(Nq - 1) * bias_sq + Nk;
+      if (ext > kBiasMaxExtent) return FA_ERR_INVALID_SHAPE;
+      bias_elems = (int64_t)ext;
+      if ((__int128)31 * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
+    }
+  }
   // a pointer may be NULL only when its buffer is empty
   if ((BH * Nq > 0 && (!Q || !O || !LSE)) || (BH > 0 && (!K || !V))) return FA_ERR_NULL_POINTER;
   // one workgroup per 128 query rows of a head; the grid has < 2^31 workgroups
@@ -62,16 +79,36 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
   if (!std::isfinite(scale)) return FA_ERR_INVALID_SCALE;
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(LSE, 4))
     return FA_ERR_UNSUPPORTED;
+  // the bias is read 16 bytes (4 keys) at a time: rows start 16-byte aligned
+  if (bias != nullptr && (!aligned(bias, 16) || bias_sb % 4 != 0 || bias_sh % 4 != 0 || bias_sq % 4 != 0))
+    return FA_ERR_UNSUPPORTED;
   const int64_t q_bytes = BH * Nq * row_bytes, kv_bytes = BH * Nk * row_bytes, l_bytes = BH * Nq * 4;
+  const int64_t b_bytes = bias_elems * 4;
   if (overlaps(O, q_bytes, Q, q_bytes) || overlaps(O, q_bytes, K, kv_bytes) || overlaps(O, q_bytes, V, kv_bytes) ||
       overlaps(LSE, l_bytes, Q, q_bytes) || overlaps(LSE, l_bytes, K, kv_bytes) ||
-      overlaps(LSE, l_bytes, V, kv_bytes) || overlaps(LSE, l_bytes, O, q_bytes))
+      overlaps(LSE, l_bytes, V, kv_bytes) || overlaps(LSE, l_bytes, O, q_bytes) ||
+      overlaps(O, q_bytes, bias, b_bytes) || overlaps(LSE, l_bytes, bias, b_bytes))
     return FA_ERR_ALIAS;
   if (BH * Nq == 0) return FA_OK;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
-  if (fa06::launch_fa_fwd(Q, K, V, O, LSE, BH, Nq, Nk, scale, causal == 1, static_cast<hipStream_t>(stream)) != 0)
-    return FA_ERR_LAUNCH;
+  fa06::LaunchArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.LSE = LSE;
+  a.BH = BH;
+  a.H = H;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale = scale;
+  a.causal = causal == 1;
+  a.bias = bias;
+  a.bias_sb = bias_sb;
+  a.bias_sh = bias_sh;
+  a.bias_sq = bias_sq;
+  if (fa06::launch_fa_fwd(a, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_LAUNCH;
   return FA_OK;
 }
 
@@ -80,17 +117,15 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
 extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                       float scale, void* stream) {
-  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, 0, nullptr, stream);
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, 0, nullptr, 0, 0, 0, stream);
 }
 
 extern "C" int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                              int causal, const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
                              int64_t bias_stride_q, void* stream) {
-  (void)bias_stride_b;
-  (void)bias_stride_h;
-  (void)bias_stride_q;
-  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, bias, stream);
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, bias, bias_stride_b, bias_stride_h,
+                             bias_stride_q, stream);
 }
 
 extern "C" const char* fa_status_string(int status) {
@@ -98,7 +133,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a pointer to a non-empty buffer is NULL";
     case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: B, H, Nq must be >= 0, Nk >= 1, and sizes must fit";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 128, N <= 2^23, pointers 16-byte aligned (LSE 4)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 128, N <= 2^23, pointers 16-byte aligned (LSE 4), "
+                                     "bias strides non-negative multiples of 4 within the addressable span";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: O or LSE overlaps Q, K, V or each other";
     case FA_ERR_INVALID_SCALE: return "FA_ERR_INVALID_SCALE: scale must be finite";
     case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no HIP device, or the current device is not gfx950";

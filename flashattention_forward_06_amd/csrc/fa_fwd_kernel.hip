@@ -24,10 +24,13 @@
 //   * V^T fragments come from the row-major V tile in LDS through
 //     ds_read_b64_tr_b16 (a transposing LDS read), so V is never transposed
 //     in memory.
-//   * K/V tiles are double buffered in LDS: tile j+1 is copied global -> LDS
-//     directly (buffer loads with the LDS destination, no registers) into
-//     the other buffer while tile j is computed (the 2-stage pipeline of the
-//     5090 article's "v3").
+//   * K/V tiles are double buffered in LDS and copied global -> LDS directly
+//     (buffer loads with the LDS destination, no registers) while the
+//     previous tiles are computed (the multi-stage pipeline of the 5090
+//     article's "v3").  Inside a wave the work is software pipelined over
+//     three tiles: iteration j computes the scores of tile j+2 and P V of
+//     tile j on the MFMAs while the VALU runs the softmax of tile j+1, so
+//     the exponentials overlap the matrix products of the same wave.
 //   * LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled per row so the
 //     K fragment reads (ds_read_b128) and the V transposing reads are free
 //     of bank conflicts (the swizzled shared memory of the 5090 article's
@@ -43,10 +46,11 @@
 //   * Workgroup ids are remapped so the q-tiles of one head run on the same
 //     XCD (workgroups are dispatched round-robin over the 8 XCDs), sharing
 //     that head's K/V in the XCD's L2.
-//   * Causal variant (the mask term of the score equation): a q-tile stops
-//     at the last K/V tile its last row can see, only tiles that cross the
+//   * Mask term of the score equation, two forms: causal (a q-tile stops at
+//     the last K/V tile its last row can see, only tiles that cross the
 //     diagonal are masked per key, and the q-tiles with the most work are
-//     dispatched first.
+//     dispatched first) and an fp32 additive bias with arbitrary broadcast
+//     strides, read straight from memory into registers one tile ahead.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -61,12 +65,12 @@ namespace {
 constexpr int D = 128;          // head size (d = d_v)
 constexpr int ROW_BYTES = D * 2; // one bf16 row
 constexpr int BR = 128;         // query rows per workgroup
-constexpr int BC = 64;          // keys per K/V tile
 constexpr int NWAVES = 4;
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int TILE_BYTES = BC * ROW_BYTES;   // one K or V tile: 16 KiB
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;  // K + V
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;   // double buffered: 64 KiB
+constexpr int Q_BYTES = BR * ROW_BYTES;      // the Q tile, staged once: 32 KiB
+// K and V tiles of BC keys, two of each in LDS (K(j+2), K(j+3), V(j), V(j+1)):
+// 64 KiB at BC = 64, which leaves room for two workgroups per CU.
+constexpr int lds_bytes(int bc) { return 4 * bc * ROW_BYTES > Q_BYTES ? 4 * bc * ROW_BYTES : Q_BYTES; }
 constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -74,6 +78,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
 typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) char lds_char;
 
 // Buffer resource: base, no stride, num_records bytes; dword3 selects the
@@ -140,15 +145,32 @@ __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char
 // Wait until this wave's outstanding global loads (incl. LDS-direct) landed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// CAUSAL: key j is hidden from query i when j > i + (Nk - Nq); tiles past a
-// q-tile's diagonal are skipped, tiles crossing it are masked per element.
-template <bool NEG_SCALE, bool CAUSAL>
+// Keeps a value live at this point, so the instructions that produce it stay
+// ahead of it (in the same basic block) instead of being sunk into a later
+// block by the compiler.
+__device__ inline void keep(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(uintx4, x))); }
+__device__ inline void keep(float x) { asm volatile("" ::"v"(x)); }
+
+constexpr float LOG2E = 1.44269504088896340736f;
+
+// One workgroup computes BR query rows of one (batch, head) against all keys.
+//   BC        keys per K/V tile (64; 32 for the bias variant, whose bias
+//             tiles live in registers)
+//   NEG_SCALE the scale is negative: the largest logit is the smallest score
+//   CAUSAL    key j is hidden from query i when j > i + (Nk - Nq); tiles past
+//             a q-tile's diagonal are skipped, tiles crossing it are masked
+//   BIAS      an fp32 bias is added to the scaled scores:
+//             bias[b*sb + h*sh + i*sq + j] (element strides)
+template <int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
+              const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H,
               int Nq, int Nk, int n_qtiles, float c_log2) {
-  __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+  constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
+  constexpr int TILE_BYTES = BC * ROW_BYTES;  // one K or V tile
+  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC)];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -202,30 +224,63 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   }
 
-  // LDS: K buffers at [0, 32K), V buffers at [32K, 64K).  K runs one tile
-  // ahead of V: while tile j's P V is accumulated, tile j+1's scores are
-  // computed, so K(j+1) and V(j) are resident together.
+  // Bias rows of this wave's 32 queries, read straight into registers: lane
+  // (c, h) needs, per 32-key block, keys 8g + 4h .. 8g + 4h + 3 (g = 0..3) of
+  // row q0 + 32*wave + c, i.e. four 16-byte loads.  The buffer ends at the
+  // last key of the wave's last valid row, so keys past Nk (and rows past
+  // Nq) read as zero; they are masked anyway.
+  __amdgpu_buffer_rsrc_t rb = make_rsrc(nullptr, 0u);
+  uint32_t bias_voff = 0;
+  if constexpr (BIAS) {
+    const int b = bh / H;
+    const int hd = bh - b * H;
+    const int qw0 = q0 + wave * 32;
+    const int nrows = Nq - qw0 < 32 ? Nq - qw0 : 32;
+    const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq;
+    const uint32_t bytes = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * bias_sq + Nk) * 4) : 0u;
+    rb = make_rsrc(base, bytes);
+    bias_voff = (uint32_t)((int64_t)c * bias_sq * 4) + 16u * (uint32_t)h;
+  }
+  auto load_bias = [&](int t, floatx4 (&bt)[KB][4]) FA_INLINE {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)t * (uint32_t)(BC * 4));
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bt[kb][g] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rb, bias_voff + (uint32_t)(kb * 128 + g * 32), soff, 0));
+  };
+
+  // LDS: two K buffers then two V buffers.  K runs two tiles ahead of V:
+  // iteration j computes the scores of tile j+2 and accumulates P V of tile
+  // j, so K(j+2) and V(j) are read while K(j+3) and V(j+1) are copied in.
   char* const kbuf0 = smem;
   char* const vbuf0 = smem + 2 * TILE_BYTES;
   auto kbuf = [&](int i) FA_INLINE { return kbuf0 + i * TILE_BYTES; };
   auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * TILE_BYTES; };
 
-  // ---- prologue: Q (staged in the V buffers), K(0), K(1).
-  tile_to_lds<BR, false>(rq, q0, vbuf0, wave_u, lane);
-  tile_to_lds<BC, false>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, false>(rk, BC, kbuf(1), wave_u, lane);
+  // ---- prologue: the Q tile through LDS into registers.
+  tile_to_lds<BR, false>(rq, q0, smem, wave_u, lane);
   wait_vmem();
   __syncthreads();
-
   bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
   {
     const uint32_t row = wave * 32 + c;
 #pragma unroll
     for (int t = 0; t < 8; ++t)
-      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(vbuf0 + k_swz(row, 2 * t + h)));
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + k_swz(row, 2 * t + h)));
   }
-  __syncthreads();  // the V buffers are reused from here on
+  __syncthreads();  // the Q staging area is reused from here on
+  tile_to_lds<BC, false>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, false>(rk, BC, kbuf(1), wave_u, lane);
   tile_to_lds<BC, true>(rv, 0, vbuf(0), wave_u, lane);
+  floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
+  if constexpr (BIAS) {
+    load_bias(0, b0);
+    if (n_tiles > 1) load_bias(1, bcur);
+  }
+  wait_vmem();
+  __syncthreads();
 
   floatx16 oacc[4];
 #pragma unroll
@@ -233,10 +288,10 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_run = -__builtin_inff();  // running max, log2 units, per query
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
-  // S^T = K Q^T for the 64 keys of one K buffer (two 32-key blocks).
-  auto scores = [&](const char* ks, floatx16 (&s)[2]) FA_INLINE {
+  // S^T = K Q^T for the BC keys of one K buffer (32-key blocks).
+  auto scores = [&](const char* ks, floatx16 (&s)[KB]) FA_INLINE {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       s[kb] = floatx16{};
       const uint32_t row = kb * 32 + c;
 #pragma unroll
@@ -247,46 +302,73 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
-  // Online softmax of one tile's scores -> P (bf16, B operand of the P V
-  // product).  Branch free: the decision to raise the running max is wave
-  // uniform (ballot); returns the factor the output accumulator must be
-  // multiplied by before this tile's P V is added (1 when unchanged).
-  // MASK tiles hide the keys above `lim` (this row's last visible key,
-  // relative to the tile's first key).
-  auto softmax = [&](floatx16 (&s)[2], bf16x8 (&pb)[4], int lim, auto mask_tag, bool& rescale) FA_INLINE -> float {
+  // Online softmax of one tile's scores -> P (bf16, the B operand of the
+  // P V product).  The decision to raise the running max is wave uniform
+  // (ballot); returns the factor the output accumulator must be multiplied
+  // by before the next P V is added (1 when unchanged).  MASK tiles hide the
+  // keys above `lim` (this row's last visible key, relative to the tile's
+  // first key).
+  auto softmax = [&](floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB], int lim,
+                     auto mask_tag, bool& rescale) FA_INLINE -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
-    if constexpr (MASK) {
+    constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;  // a row may see no key (yet)
+    float m_tile;
+    if constexpr (BIAS) {
+      // logits in log2 units: scale*log2(e)*s + log2(e)*bias
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
+          float t = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
+          if constexpr (MASK) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > lim) t = -__builtin_inff();
+          }
+          s[kb][r] = t;
         }
+      float ext = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[kb][r]);
+      m_tile = wave_max_halves(ext);
+    } else {
+      if constexpr (MASK) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > lim) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
+          }
+      }
+      float ext = s[0][0];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
+      ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
+      m_tile = ext * c_log2;
     }
-    float ext = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
-    ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
-    const float m_tile = ext * c_log2;
     rescale = __ballot(m_tile > m_run + RESCALE_SLACK) != 0;
     const float m_new = rescale ? fmaxf(m_run, m_tile) : m_run;
     float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    // a causal row that has seen no key yet keeps m = -inf (and l = 0)
-    if constexpr (CAUSAL) alpha = m_new == -__builtin_inff() ? 1.0f : alpha;
+    // a row that has seen no key yet keeps m = -inf, l = 0 and O = 0; it
+    // subtracts 0 instead, so its hidden keys give exp2(-inf) = 0, not NaN
+    float m_use = m_new;
+    if constexpr (CAN_BE_EMPTY) {
+      const bool empty = m_new == -__builtin_inff();
+      alpha = empty ? 1.0f : alpha;
+      m_use = empty ? 0.0f : m_new;
+    }
     m_run = m_new;
     float lsum = 0.0f;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
-        if constexpr (MASK) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) p = 0.0f;
-        }
+        const float x = BIAS ? s[kb][r] - m_use : __builtin_fmaf(s[kb][r], c_log2, -m_use);
+        const float p = __builtin_amdgcn_exp2f(x);
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
@@ -294,8 +376,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return alpha;
   };
 
-  // O^T += V^T P^T for the 64 keys of one V buffer: 4 d-blocks x 4 key steps.
-  auto accumulate = [&](const char* vs, const bf16x8 (&pb)[4]) FA_INLINE {
+  // O^T += V^T P^T for the BC keys of one V buffer: 4 d-blocks x 2*KB key steps.
+  auto accumulate = [&](const char* vs, const bf16x8 (&pb)[2 * KB]) FA_INLINE {
     const int g = lane >> 4;          // 16-lane group
     const int i16 = lane & 15;
     const int sub = i16 >> 2;         // which of the 4 keys this lane addresses
@@ -307,7 +389,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const uint32_t ch = (uint32_t)d0 >> 3;
       const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
 #pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
+      for (int ks4 = 0; ks4 < 2 * KB; ++ks4) {
         const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
         const uint32_t r1 = r0 + 8;
         const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -331,45 +413,68 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
   };
 
-  // ---- tile 0: scores and softmax before the loop.
-  bf16x8 pb[4];
+  // ---- tiles 0 and 1: P(0) and S(1) before the loop.
+  bf16x8 pb[2 * KB];  // P of the tile whose P V is next
+  floatx16 s1[KB];    // scores of the tile whose softmax is next
   {
-    floatx16 s[2];
-    scores(kbuf(0), s);
+    floatx16 s0[KB];
+    scores(kbuf(0), s0);
     bool rs;
     if (first_masked == 0)
-      softmax(s, pb, key_lim, std::true_type{}, rs);
+      softmax(s0, b0, pb, key_lim, std::true_type{}, rs);
     else
-      softmax(s, pb, key_lim, std::false_type{}, rs);
+      softmax(s0, b0, pb, key_lim, std::false_type{}, rs);
     // O is still zero: no rescale needed
+    if (n_tiles > 1) scores(kbuf(1), s1);
   }
+  __syncthreads();  // K(0) consumed: K(2) goes into its buffer
+  if (n_tiles > 2) tile_to_lds<BC, false>(rk, 2 * BC, kbuf(0), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
-  // Iteration j: P(j) V(j) accumulated while S(j+1) is computed and turned
-  // into P(j+1).  On entry K(j+1) is in kbuf((j+1)&1), V(j) in vbuf(j&1);
-  // the iteration prefetches K(j+2) into kbuf(j&1) and V(j+1) into
-  // vbuf((j+1)&1), whose previous contents were consumed before the last
-  // barrier.
-  auto iteration = [&](int j, auto par_tag, auto has_next_tag, auto mask_next_tag) FA_INLINE {
+  // Iteration j: three independent pieces of work, so the VALU softmax
+  // overlaps the MFMAs of the same wave:
+  //   S(j+2) = K(j+2) Q^T  (MFMA; K(j+2) in kbuf(j&1))      if HAS_S2
+  //   softmax of tile j+1, scores computed one iteration earlier (VALU)
+  //                                                         if HAS_S1
+  //   O += P(j) V(j)       (MFMA; V(j) in vbuf(j&1))
+  // while K(j+3) and V(j+1) are copied into the other buffers (and the bias
+  // of tile j+2 into registers).  The output is rescaled after P(j) V(j),
+  // before P(j+1) V(j+1) joins it.
+  floatx4 bnext[KB][4];
+  auto iteration = [&](int j, auto par_tag, auto has_s2_tag, auto has_s1_tag, auto mask1_tag) FA_INLINE {
     constexpr int P = decltype(par_tag)::value;  // == j & 1
-    constexpr bool HAS_NEXT = decltype(has_next_tag)::value;
-    if (j + 2 < n_tiles) tile_to_lds<BC, false>(rk, (j + 2) * BC, kbuf(P), wave_u, lane);
-    if (HAS_NEXT) tile_to_lds<BC, true>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_NEXT) {
-      floatx16 s[2];
-      scores(kbuf(P ^ 1), s);
-      bf16x8 pn[4];
-      bool rs;
-      const float alpha = softmax(s, pn, key_lim - (j + 1) * BC, mask_next_tag, rs);
-      accumulate(vbuf(P), pb);
+    constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
+    constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
+    if (j + 3 < n_tiles) tile_to_lds<BC, false>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, true>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
+    floatx16 s2[KB];
+    if constexpr (HAS_S2) scores(kbuf(P), s2);
+    bf16x8 pn[2 * KB];
+    bool rs = false;
+    float alpha = 1.0f;
+    if constexpr (HAS_S1) alpha = softmax(s1, bcur, pn, key_lim - (j + 1) * BC, mask1_tag, rs);
+    accumulate(vbuf(P), pb);
+    if constexpr (HAS_S1) {
+#pragma unroll
+      for (int i = 0; i < 2 * KB; ++i) keep(pn[i]);
+      keep(l_run);
       if (rs) rescale_o(alpha);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = pn[i];
+      for (int i = 0; i < 2 * KB; ++i) pb[i] = pn[i];
+      if constexpr (HAS_S2) {
+#pragma unroll
+        for (int i = 0; i < KB; ++i) s1[i] = s2[i];
+        if constexpr (BIAS) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) bcur[kb][g] = bnext[kb][g];
+        }
+      }
       wait_vmem();
       __syncthreads();
-    } else {
-      accumulate(vbuf(P), pb);
     }
   };
 
@@ -377,56 +482,47 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   using P1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
-  if constexpr (!CAUSAL) {
-    // iterations 0 .. n_tiles-3 compute S of a full tile
-    int j = 0;
-    for (; j + 1 < n_tiles - 2; j += 2) {
-      iteration(j, P0{}, T{}, F{});
-      iteration(j + 1, P1{}, T{}, F{});
-    }
-    if (j < n_tiles - 2) {
-      iteration(j, P0{}, T{}, F{});
+  // Iterations j in [j0, j1) with S(j+2) and the same masking of tile j+1;
+  // the buffer parity (j & 1) is a compile-time constant of each
+  // instantiation, so the loop is unrolled by two.
+  auto run = [&](int j0, int j1, auto mask_tag) FA_INLINE {
+    int j = j0;
+    if (j < j1 && (j & 1)) {
+      iteration(j, P1{}, T{}, T{}, mask_tag);
       ++j;
     }
-    // iteration n_tiles-2 computes S of the last tile (masked if partial)
-    if (j == n_tiles - 2) {
-      const bool tail = first_masked < n_tiles;
-      if (j & 1) {
-        if (tail) iteration(j, P1{}, T{}, T{}); else iteration(j, P1{}, T{}, F{});
-      } else {
-        if (tail) iteration(j, P0{}, T{}, T{}); else iteration(j, P0{}, T{}, F{});
-      }
+    for (; j + 1 < j1; j += 2) {
+      iteration(j, P0{}, T{}, T{}, mask_tag);
+      iteration(j + 1, P1{}, T{}, T{}, mask_tag);
     }
-  } else {
-    // Iterations j in [j0, j1) all compute S of a next tile with the same
-    // masking; the K/V buffer parity (j & 1) is a compile-time constant of
-    // each instantiation, so the loop is unrolled by two.
-    auto run = [&](int j0, int j1, auto mask_tag) FA_INLINE {
-      int j = j0;
-      if (j < j1 && (j & 1)) {
-        iteration(j, P1{}, T{}, mask_tag);
-        ++j;
-      }
-      for (; j + 1 < j1; j += 2) {
-        iteration(j, P0{}, T{}, mask_tag);
-        iteration(j + 1, P1{}, T{}, mask_tag);
-      }
-      if (j < j1) iteration(j, P0{}, T{}, mask_tag);
-    };
-    // the next tile is unmasked for j + 1 < first_masked, masked from there on
-    // (only the few tiles that cross the diagonal or hold the Nk tail)
-    int j_split = first_masked - 1;
-    j_split = j_split < 0 ? 0 : (j_split > n_tiles - 1 ? n_tiles - 1 : j_split);
-    run(0, j_split, F{});
-    run(j_split, n_tiles - 1, T{});
+    if (j < j1) iteration(j, P0{}, T{}, T{}, mask_tag);
+  };
+  // tile j+1 needs masks from first_masked on: at most the last tile
+  // (ragged Nk) without CAUSAL, the tiles crossing the diagonal with it
+  const int j_end = n_tiles - 2 > 0 ? n_tiles - 2 : 0;
+  int j_split = first_masked - 1;
+  j_split = j_split < 0 ? 0 : (j_split > j_end ? j_end : j_split);
+  run(0, j_split, F{});
+  if constexpr (CAUSAL) run(j_split, j_end, T{});
+  // iteration n_tiles-2: no S(j+2); the softmax of the last tile
+  if (n_tiles >= 2) {
+    const int j = n_tiles - 2;
+    const bool mask = n_tiles - 1 >= first_masked;
+    if (j & 1) {
+      if (mask) iteration(j, P1{}, F{}, T{}, T{}); else iteration(j, P1{}, F{}, T{}, F{});
+    } else {
+      if (mask) iteration(j, P0{}, F{}, T{}, T{}); else iteration(j, P0{}, F{}, T{}, F{});
+    }
   }
   // last iteration: P V of the last tile only
-  if ((n_tiles - 1) & 1) iteration(n_tiles - 1, P1{}, F{}, F{}); else iteration(n_tiles - 1, P0{}, F{}, F{});
+  if ((n_tiles - 1) & 1) iteration(n_tiles - 1, P1{}, F{}, F{}, F{}); else iteration(n_tiles - 1, P0{}, F{}, F{}, F{});
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
   const float l_tot = wave_sum_halves(l_run);
-  // l = 0 only for a causal row that sees no key: O = 0, LSE = -inf
-  const float inv_l = (CAUSAL && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
+  // l = 0 only for a row that sees no key (causal or all-(-inf) bias):
+  // O = 0, LSE = -inf
+  constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;
+  const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
   const int q = q0 + wave * 32 + c;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb)
@@ -446,33 +542,52 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   if (h == 0 && q < Nq) {
     const float ln2 = 0.69314718055994530942f;
-    LSE[(size_t)bh * Nq + q] = (CAUSAL && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * ln2;
+    LSE[(size_t)bh * Nq + q] = (CAN_BE_EMPTY && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * ln2;
   }
+}
+
+template <int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+const void* kernel_ptr() {
+  return (const void*)&fa_fwd_kernel<BC, NEG_SCALE, CAUSAL, BIAS>;
 }
 
 }  // namespace
 
-int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                  int64_t BH, int64_t Nq, int64_t Nk, float scale, bool causal, hipStream_t stream) {
-  const int n_qtiles = (int)((Nq + BR - 1) / BR);
-  const int64_t nblk = BH * n_qtiles;
-  const float c_log2 = (float)((double)scale * 1.4426950408889634074);
-  const uint16_t* q = static_cast<const uint16_t*>(Q);
-  const uint16_t* k = static_cast<const uint16_t*>(K);
-  const uint16_t* v = static_cast<const uint16_t*>(V);
-  uint16_t* o = static_cast<uint16_t*>(O);
-  int nq = (int)Nq, nk = (int)Nk;
-  void* args[] = {&q, &k, &v, &o, &LSE, &nq, &nk, (void*)&n_qtiles, (void*)&c_log2};
-  const bool neg = scale < 0.0f;
-  const void* fn = causal ? (neg ? (const void*)&fa_fwd_kernel<true, true> : (const void*)&fa_fwd_kernel<false, true>)
-                          : (neg ? (const void*)&fa_fwd_kernel<true, false> : (const void*)&fa_fwd_kernel<false, false>);
+int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
+  const int n_qtiles = (int)((a.Nq + BR - 1) / BR);
+  const int64_t nblk = a.BH * n_qtiles;
+  const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
+  const uint16_t* q = static_cast<const uint16_t*>(a.Q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.K);
+  const uint16_t* v = static_cast<const uint16_t*>(a.V);
+  uint16_t* o = static_cast<uint16_t*>(a.O);
+  float* lse = a.LSE;
+  const float* bias = a.bias;
+  int64_t sb = a.bias_sb, sh = a.bias_sh, sq = a.bias_sq;
+  int heads = (int)a.H;
+  int nq = (int)a.Nq, nk = (int)a.Nk;
+  int nqt = n_qtiles;
+  float cl = c_log2;
+  void* args[] = {&q, &k, &v, &o, &lse, &bias, &sb, &sh, &sq, &heads, &nq, &nk, &nqt, &cl};
+  const bool neg = a.scale < 0.0f;
+  const void* fn;
+  if (bias) {
+    // the sign of the scale needs no variant here: the max is taken over the
+    // biased logits themselves
+    fn = a.causal ? kernel_ptr<32, false, true, true>() : kernel_ptr<32, false, false, true>();
+  } else if (a.causal) {
+    fn = neg ? kernel_ptr<64, true, true, false>() : kernel_ptr<64, false, true, false>();
+  } else {
+    fn = neg ? kernel_ptr<64, true, false, false>() : kernel_ptr<64, false, false, false>();
+  }
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v3.1: BR=128 (4 waves x 32 rows), BC=64, K one tile ahead of V, direct-to-LDS, "
-         "S^T=K.Q^T on mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16; causal variant with tile skipping";
+  return "gfx950 fa_fwd v4: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+         "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16, "
+         "V^T via ds_read_b64_tr_b16; causal tile skipping; fp32 additive bias";
 }
 
 }  // namespace fa06

@@ -4,10 +4,23 @@
 #include <stdint.h>
 
 namespace fa06 {
-// Enqueue the forward kernel for BH = B*H independent heads (causal: key j
-// hidden from query i when j > i + Nk - Nq).  Arguments are already validated
-// by the caller.  Returns 0 or the hipError_t of the launch.
-int launch_fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
-                  int64_t BH, int64_t Nq, int64_t Nk, float scale, bool causal, hipStream_t stream);
+
+// One forward call over BH = B*H independent heads, already validated.
+struct LaunchArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  float* LSE;
+  int64_t BH, H, Nq, Nk;
+  float scale;
+  bool causal;          // key j hidden from query i when j > i + Nk - Nq
+  const float* bias;    // NULL, or fp32 bias[b*bias_sb + h*bias_sh + i*bias_sq + j]
+  int64_t bias_sb, bias_sh, bias_sq;
+};
+
+// Enqueues the kernel; returns 0 or the hipError_t of the launch.
+int launch_fa_fwd(const LaunchArgs& args, hipStream_t stream);
 const char* kernel_config_string();
+
 }  // namespace fa06

@@ -58,20 +58,50 @@ def test_validation_codes(kw, code):
     assert call(**kw) == code
 
 
-def call_masked(causal=1, bias=None, **kw):
+def call_masked(causal=1, bias=None, sb=0, sh=0, sq=0, **kw):
     a = {**GOOD, **kw}
     return fa.fa_fwd_masked_raw(Qp, Kp, Vp, Op, Lp, a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"],
-                                causal, bias, 0, 0, 0, 0)
+                                causal, bias, sb, sh, sq, 0)
+
+
+BIAS_P = 0x60000000  # a 16-byte aligned address clear of the other fake buffers
 
 
 def test_masked_entry_validation():
     assert call_masked(causal=2) == 3
     assert call_masked(causal=-1) == 3
-    assert call_masked(bias=0x60000000) == 3      # additive bias is not in this build
     assert call_masked(Nk=0) == 2
     assert call_masked(d=64) == 3
     assert call_masked(scale=float("nan")) == 5
     assert call_masked(Nq=0) == 0
+    assert call_masked(Nq=0, bias=BIAS_P) == 0          # empty problem: no-op
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bias=BIAS_P + 4), 3),                         # base not 16-byte aligned
+    (dict(bias=BIAS_P, sq=258), 3),                     # row stride not a multiple of 4
+    (dict(bias=BIAS_P, sh=6, sq=256), 3),
+    (dict(bias=BIAS_P, sb=2, sq=256), 3),
+    (dict(bias=BIAS_P, sq=-256), 3),                    # negative strides
+    (dict(bias=BIAS_P, sh=-4), 3),
+    (dict(bias=BIAS_P, sq=1 << 25), 3),                 # 32 rows span more than 2^29 elements
+    (dict(bias=BIAS_P, sb=1 << 62, B=3), 2),            # extent beyond 2^60 elements
+    (dict(bias=Op - 4096, sq=256), 4),                  # bias rows overlap O
+    (dict(bias=Lp, sq=0), 4),                           # bias overlaps LSE
+    (dict(bias=Qp, sq=256), -1),                        # reading Q as bias is allowed
+    (dict(bias=BIAS_P, sq=256, sh=256 * 256), -1),      # valid: fails only at the device check
+    (dict(bias=BIAS_P, causal=0), -1),                  # broadcast over everything, no causal mask
+])
+def test_bias_validation(kw, code):
+    if code == -1:
+        # arguments accepted: without a GPU the call stops at the device
+        # check; with one it would launch on these fake addresses, so skip
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("would launch on fake pointers")
+        assert call_masked(**kw) == 6
+    else:
+        assert call_masked(**kw) == code
 
 
 def test_empty_problem_is_noop():
