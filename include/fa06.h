@@ -95,13 +95,22 @@ int fa_fwd(const void *Q, const void *K, const void *V, void *O, float *LSE,
  *   causal   0 or 1.  With 1, key j is hidden from query i when
  *            j > i + (Nk - Nq): the diagonal is aligned to the last query and
  *            the last key (for Nq = Nk, row i sees keys 0..i).  Key tiles that
- *            lie entirely past a query tile's diagonal are skipped.  A row that
- *            sees no key (only when Nq > Nk) gets O = 0 and LSE = -inf.
- *   bias     additive fp32 bias, added to scale * q_i . k_j in natural-log
- *            units; element (b, h, i, j) is bias[b*bias_stride_b +
- *            h*bias_stride_h + i*bias_stride_q + j].  Must be NULL in this
- *            build (a non-NULL bias returns FA_ERR_UNSUPPORTED); the strides
- *            are then ignored.
+ *            lie entirely past a query tile's diagonal are skipped.
+ *   bias     NULL (no bias), or a device pointer to an fp32 additive bias,
+ *            added to scale * q_i . k_j (natural-log units) before the
+ *            softmax; element (b, h, i, j) is bias[b*bias_stride_b +
+ *            h*bias_stride_h + i*bias_stride_q + j] (element strides; a zero
+ *            stride broadcasts over that dimension; keys are contiguous).  A
+ *            -inf entry hides its key.  Read only; it may alias Q, K or V but
+ *            not O or LSE (FA_ERR_ALIAS).  Requirements, else
+ *            FA_ERR_UNSUPPORTED: the pointer is 16-byte aligned, the three
+ *            strides are >= 0 and multiples of 4, and 31*bias_stride_q + Nk +
+ *            128 <= 2^29 (32 consecutive rows are addressed with 32-bit byte
+ *            offsets).  An extent (B-1)*sb + (H-1)*sh + (Nq-1)*sq + Nk above
+ *            2^60 elements returns FA_ERR_INVALID_SHAPE.  With bias == NULL
+ *            the strides are ignored.
+ *   A row that sees no key (causal with Nq > Nk, or -inf bias on every key
+ *   it could see) gets O = 0 and LSE = -inf.
  *   other arguments, ownership, execution and errors as for fa_fwd; a causal
  *   value other than 0 or 1 returns FA_ERR_UNSUPPORTED.
  */
