@@ -11,6 +11,8 @@ as defined in "FlashAttention'ı Anlamak Bölüm 1", section 0.2 "Notasyon"
 additive bias and/or a causal mask), evaluated row by row in fp64 from the
 bf16 input bits.  Outputs: O in fp64 (never rounded to bf16) and the
 natural-log log-sum-exp of the scaled (and biased) logits per query row.
+The backward pass (dQ, dK, dV of a loss through O, given dO) is the chain
+rule of the same equations, also in fp64 (``attention_bwd*``).
 """
 from __future__ import annotations
 
@@ -60,6 +62,16 @@ def _lib():
                                                 ctypes.c_float, ctypes.c_int, _p, _i64, _i64, _i64,
                                                 _p, _i64, _p, _p]
         lib.oracle_attn_masked_fp64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_fp64.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                             ctypes.c_float, ctypes.c_int, _p, _i64, _i64, _i64,
+                                             _p, _p, _p, _p, _p]
+        lib.oracle_attn_bwd_fp64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_dq_rows_fp64.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                     ctypes.c_float, ctypes.c_int, _p, _i64, _p]
+        lib.oracle_attn_bwd_dq_rows_fp64.restype = ctypes.c_int
+        lib.oracle_attn_bwd_dkdv_keys_fp64.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                                       ctypes.c_float, ctypes.c_int, _p, _i64, _p, _p]
+        lib.oracle_attn_bwd_dkdv_keys_fp64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
         _lib_handle = lib
@@ -146,6 +158,79 @@ def attention_masked(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float, 
     if rc != 0:
         raise ValueError(f"oracle_attn_masked_fp64 failed with code {rc}")
     return O, LSE
+
+
+def _bias_view(bias, B, H, Nq, Nk):
+    if bias is None:
+        return None, 0, 0, 0, None
+    bias = np.asarray(bias, dtype=np.float32)
+    full = np.broadcast_to(bias, (B, H, Nq, Nk))
+    if full.strides[3] != 4:
+        bias = np.ascontiguousarray(bias)
+        full = np.broadcast_to(bias, (B, H, Nq, Nk))
+    sb, sh, sq = (st // 4 for st in full.strides[:3])
+    return full.ctypes.data, sb, sh, sq, full
+
+
+def _check_dO(dO, B, H, Nq, dv):
+    if dO.dtype != np.uint16 or dO.shape != (B, H, Nq, dv):
+        raise TypeError(f"dO must be uint16 bf16 bits of shape {(B, H, Nq, dv)}, got {dO.dtype} {dO.shape}")
+    return np.ascontiguousarray(dO)
+
+
+def attention_bwd(Q, K, V, dO, scale: float, causal: bool = False, bias=None):
+    """Gradients of sum(O * dO) for the attention of ``attention_masked``.
+
+    Returns (dQ [B,H,Nq,d], dK [B,H,Nk,d], dV [B,H,Nk,dv], D [B,H,Nq], LSE
+    [B,H,Nq]), all fp64; D_i = sum_j P_ij dP_ij.
+    """
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    dO = _check_dO(dO, B, H, Nq, dv)
+    bias_ptr, sb, sh, sq, _keep = _bias_view(bias, B, H, Nq, Nk)
+    dQ = np.empty((B, H, Nq, d))
+    dK = np.empty((B, H, Nk, d))
+    dV = np.empty((B, H, Nk, dv))
+    D = np.empty((B, H, Nq))
+    LSE = np.empty((B, H, Nq))
+    rc = _lib().oracle_attn_bwd_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
+                                     B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
+                                     bias_ptr, sb, sh, sq, dQ.ctypes.data, dK.ctypes.data, dV.ctypes.data,
+                                     D.ctypes.data, LSE.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_fp64 failed with code {rc}")
+    return dQ, dK, dV, D, LSE
+
+
+def attention_bwd_dq_rows(Q, K, V, dO, scale: float, rows, causal: bool = False):
+    """dQ of selected query rows (flat indices into [B*H*Nq]): [n, d] fp64."""
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    dO = _check_dO(dO, B, H, Nq, dv)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    dQ = np.empty((rows.shape[0], d))
+    rc = _lib().oracle_attn_bwd_dq_rows_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
+                                             B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
+                                             rows.ctypes.data, rows.shape[0], dQ.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_dq_rows_fp64 failed with code {rc}")
+    return dQ
+
+
+def attention_bwd_dkdv_keys(Q, K, V, dO, scale: float, keys, causal: bool = False):
+    """dK and dV of selected keys (flat indices into [B*H*Nk]): ([n, d], [n, dv]) fp64."""
+    B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
+    Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
+    dO = _check_dO(dO, B, H, Nq, dv)
+    keys = np.ascontiguousarray(keys, dtype=np.int64)
+    dK = np.empty((keys.shape[0], d))
+    dV = np.empty((keys.shape[0], dv))
+    rc = _lib().oracle_attn_bwd_dkdv_keys_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
+                                               B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
+                                               keys.ctypes.data, keys.shape[0], dK.ctypes.data, dV.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_attn_bwd_dkdv_keys_fp64 failed with code {rc}")
+    return dK, dV
 
 
 def max_threads() -> int:

@@ -24,8 +24,9 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "fa_oracle.c")
 MUTATIONS = {
     "scale dropped": ("s[j] = sigma * dot;", "s[j] = dot;"),
     "exp sign flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(s[j] + m);"),
-    "K transposed": ("widen_bf16(K[j * d + c])", "widen_bf16(K[c * n_vis + j])"),
-    "LSE max term dropped": ("*lse = m + log(l);", "*lse = log(l);"),
+    "K transposed": ("widen_bf16(K[j * d + c]);\n        s[j] = sigma * dot;",
+                     "widen_bf16(K[c * n_vis + j]);\n        s[j] = sigma * dot;"),
+    "LSE max term dropped": ("    *lse = m + log(l);\n}", "    *lse = log(l);\n}"),
     "no normalisation": ("for (int64_t c = 0; c < dv; ++c) o[c] /= l;", ""),
     "always head 0": ("const int64_t bh = flat / Nq;", "const int64_t bh = 0;"),
     "Q ignores head": ("attend_one_row(Q + flat * d,", "attend_one_row(Q + (flat % Nq) * d,"),
@@ -40,7 +41,30 @@ MASK_MUTATIONS = {
     "causal diagonal off by one": ("n_vis = i + (Nk - Nq) + 1;", "n_vis = i + (Nk - Nq);"),
     "causal diagonal not aligned to the last key": ("n_vis = i + (Nk - Nq) + 1;", "n_vis = i + 1;"),
     "bias subtracted": ("if (bias_row) s[j] += (double)bias_row[j];", "if (bias_row) s[j] -= (double)bias_row[j];"),
-    "bias head stride ignored": ("(bh % H) * bias_sh", "0 * bias_sh"),
+    "bias head stride ignored": ("(bh % H) * sh", "0 * sh"),
+}
+
+
+# Mistakes in the backward pass, caught by finite differences of an
+# independent forward (tests/test_oracle_bwd.py).
+BWD_MUTATIONS = {
+    "softmax Jacobian term D dropped": (
+        "const double ds = p[j] * (dp[j] - Di);\n                    for (int64_t c = 0; c < d; ++c) {\n"
+        "                        dQi[c]",
+        "const double ds = p[j] * dp[j];\n                    for (int64_t c = 0; c < d; ++c) {\n"
+        "                        dQi[c]"),
+    "dK without the scale": ("dKh[j * d + c] += sigma * ds * widen_bf16(qi[c]);",
+                             "dKh[j * d + c] += ds * widen_bf16(qi[c]);"),
+    "dK from K instead of Q": ("dKh[j * d + c] += sigma * ds * widen_bf16(qi[c]);",
+                               "dKh[j * d + c] += sigma * ds * widen_bf16(Kh[j * d + c]);"),
+    "dV weighted by dP instead of P": ("dVh[j * dv + c] += p[j] * widen_bf16(dOi[c]);",
+                                       "dVh[j * dv + c] += dp[j] * widen_bf16(dOi[c]);"),
+    "D not weighted by P": ("Di += p[j] * dot;", "Di += dot;"),
+    "probabilities not normalised": ("for (int64_t j = 0; j < n_vis; ++j) p[j] /= l;", ""),
+    "backward scores from a transposed K": ("widen_bf16(K[j * d + c]);\n        p[j] = sigma * dot;",
+                                            "widen_bf16(K[c * n_vis + j]);\n        p[j] = sigma * dot;"),
+    "dP ignores the value row": ("dot += widen_bf16(dOi[c]) * widen_bf16(V[j * dv + c]);",
+                                 "dot += widen_bf16(dOi[c]) * widen_bf16(V[c]);"),
 }
 
 
@@ -59,6 +83,9 @@ def build_mutant(tmp_path, name, old, new):
     so.oracle_attn_masked_fp64.argtypes = [p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                            ctypes.c_int, p, i64, i64, i64, p, i64, p, p]
     so.oracle_attn_masked_fp64.restype = ctypes.c_int
+    so.oracle_attn_bwd_fp64.argtypes = [p, p, p, p, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                        ctypes.c_int, p, i64, i64, i64, p, p, p, p, p]
+    so.oracle_attn_bwd_fp64.restype = ctypes.c_int
 
     def attention(Q, K, V, scale):
         B, H, Nq, d = Q.shape
@@ -82,7 +109,18 @@ def build_mutant(tmp_path, name, old, new):
                                         H * Nq * Nk, Nq * Nk, Nk, None, B * H * Nq, O.ctypes.data, L.ctypes.data)
         assert rc == 0
         return O, L
+    def bwd(Q, K, V, dO, scale, causal=False):
+        B, H, Nq, d = Q.shape
+        Nk, dv = K.shape[2], V.shape[3]
+        out = [np.empty((B, H, Nq, d)), np.empty((B, H, Nk, d)), np.empty((B, H, Nk, dv)),
+               np.empty((B, H, Nq)), np.empty((B, H, Nq))]
+        rc = so.oracle_attn_bwd_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
+                                     B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(causal), None, 0, 0, 0,
+                                     *(a.ctypes.data for a in out))
+        assert rc == 0
+        return out
     attention.masked = masked
+    attention.bwd = bwd
     return attention
 
 
@@ -153,3 +191,28 @@ def test_mask_mutant_is_caught(tmp_path, name):
 def test_unmutated_oracle_passes_the_masked_pins(tmp_path):
     attention = build_mutant(tmp_path, "none", "int oracle_max_threads(void)", "int oracle_max_threads(void)")
     assert masked_pins_pass(attention.masked)
+
+
+def bwd_pins_pass(bwd):
+    """Finite differences of an independent fp64 forward, causal and not."""
+    from tests.test_oracle_bwd import finite_diff
+    ok = True
+    for causal, seed in ((False, 30), (True, 31)):
+        Q, K, V = fi.make_qkv(1, 2, 4, 5, 8, seed=seed)
+        dO = fi.make_qkv(1, 2, 4, 1, 8, seed=seed + 1)[0]
+        dQ, dK, dV, _, _ = bwd(Q, K, V, dO, 0.4, causal)
+        gQ, gK, gV = finite_diff(widen(Q), widen(K), widen(V), widen(dO), np.float64(np.float32(0.4)), causal, None)
+        ok &= all(np.allclose(a, b, rtol=0, atol=2e-7) for a, b in ((dQ, gQ), (dK, gK), (dV, gV)))
+    return bool(ok)
+
+
+def test_unmutated_oracle_passes_the_backward_pins(tmp_path):
+    attention = build_mutant(tmp_path, "none", "int oracle_max_threads(void)", "int oracle_max_threads(void)")
+    assert bwd_pins_pass(attention.bwd)
+
+
+@pytest.mark.parametrize("name", list(BWD_MUTATIONS))
+def test_backward_mutant_is_caught(tmp_path, name):
+    old, new = BWD_MUTATIONS[name]
+    attention = build_mutant(tmp_path, name, old, new)
+    assert not bwd_pins_pass(attention.bwd), f"mutation {name!r} was not detected by any pin"
