@@ -66,6 +66,11 @@ def load_library(path: str | None = None):
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_build_info.argtypes = []
     lib.fa_build_info.restype = ctypes.c_char_p
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                           ctypes.c_int, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_build_info.argtypes = []
+    lib.fa_bwd_build_info.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -77,6 +82,18 @@ def fa_status_string(status: int) -> str:
 
 def fa_build_info() -> str:
     return load_library().fa_build_info().decode()
+
+
+def fa_bwd_build_info() -> str:
+    return load_library().fa_bwd_build_info().decode()
+
+
+def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int,
+               dq_ptr: int, dk_ptr: int, dv_ptr: int, delta_ptr: int,
+               B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int, stream: int) -> int:
+    """Direct call of the C ``fa_bwd`` on raw device pointers; returns the status."""
+    return load_library().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr,
+                                 B, H, Nq, Nk, d, ctypes.c_float(scale), int(causal), stream)
 
 
 def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
@@ -187,5 +204,54 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
     return out, lse
 
 
-__all__ = ["fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
+           dq=None, dk=None, dv=None, delta=None):
+    """Attention backward on torch tensors: gradients of a loss through O.
+
+    q, k, v, o, do: bf16 [B, H, N, 128] contiguous on one HIP device (o and
+    lse are the outputs of ``fa_fwd`` for the same q, k, v, scale and causal
+    flag; lse fp32 [B, H, Nq]).  Returns ``(dq, dk, dv)`` in bf16, plus the
+    fp32 ``delta`` workspace [B, H, Nq] (D_i = dO_i . O_i) as a fourth value.
+    Optional output tensors of those shapes are written in place.
+    """
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise TypeError(f"{name} must be a 4-D bfloat16 torch.Tensor")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous on q's HIP device")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d) or tuple(o.shape) != (B, H, Nq, d) \
+            or tuple(do.shape) != (B, H, Nq, d):
+        raise ValueError("shape mismatch among q, k, v, o, do")
+    if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) \
+            or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, Nq] on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+
+    def out(t, like, dtype):
+        if t is None:
+            return torch.empty(like, dtype=dtype, device=q.device)
+        if t.dtype != dtype or tuple(t.shape) != tuple(like) or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"output tensor must be contiguous {dtype} {tuple(like)} on q's device")
+        return t
+
+    dq = out(dq, (B, H, Nq, d), torch.bfloat16)
+    dk = out(dk, (B, H, Nk, d), torch.bfloat16)
+    dv = out(dv, (B, H, Nk, d), torch.bfloat16)
+    delta = out(delta, (B, H, Nq), torch.float32)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                        B, H, Nq, Nk, d, float(scale), int(bool(causal)), stream)
+    if rc != 0:
+        raise FaError(rc, fa_status_string(rc))
+    return dq, dk, dv, delta
+
+
+__all__ = ["fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS"]

@@ -128,6 +128,62 @@ extern "C" int fa_fwd_masked(const void* Q, const void* K, const void* V, void* 
                              bias_stride_q, stream);
 }
 
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
+                      int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* stream) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
+  if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
+  if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
+  const int64_t BH = B * H;
+  const int64_t row_bytes = FA_HEAD_DIM * 2;
+  if (BH > (INT64_MAX / row_bytes) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
+  const bool has_q = BH * Nq > 0, has_k = BH > 0;
+  if ((has_q && (!Q || !O || !dO || !LSE || !dQ || !D)) || (has_k && (!K || !V || !dK || !dV)))
+    return FA_ERR_NULL_POINTER;
+  // one workgroup per 128 query rows (dQ) and per 128 keys (dK, dV) of a head
+  if (BH * ((Nq + 127) / 128) > INT32_MAX || BH * ((Nk + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_SCALE;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
+      !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4) || !aligned(D, 4))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t q_bytes = BH * Nq * row_bytes, kv_bytes = BH * Nk * row_bytes, l_bytes = BH * Nq * 4;
+  struct Buf {
+    const void* p;
+    int64_t n;
+  };
+  const Buf ins[] = {{Q, q_bytes}, {K, kv_bytes}, {V, kv_bytes}, {O, q_bytes}, {dO, q_bytes}, {LSE, l_bytes}};
+  const Buf outs[] = {{dQ, q_bytes}, {dK, kv_bytes}, {dV, kv_bytes}, {D, l_bytes}};
+  for (const Buf& o : outs) {
+    for (const Buf& i : ins)
+      if (overlaps(o.p, o.n, i.p, i.n)) return FA_ERR_ALIAS;
+    for (const Buf& o2 : outs)
+      if (&o2 != &o && overlaps(o.p, o.n, o2.p, o2.n)) return FA_ERR_ALIAS;
+  }
+  if (BH == 0) return FA_OK;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  fa06::BwdArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.LSE = LSE;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.Dws = D;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.scale = scale;
+  a.causal = causal == 1;
+  if (fa06::launch_fa_bwd(a, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -144,3 +200,5 @@ extern "C" const char* fa_status_string(int status) {
 }
 
 extern "C" const char* fa_build_info(void) { return fa06::kernel_config_string(); }
+
+extern "C" const char* fa_bwd_build_info(void) { return fa06::bwd_config_string(); }

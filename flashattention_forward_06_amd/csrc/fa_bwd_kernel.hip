@@ -1,0 +1,402 @@
+// fa_bwd_kernel.hip -- gfx950 (CDNA4) attention backward kernels.
+//
+// Gradients of a loss through O = softmax_row(scale * Q K^T) V, given dO,
+// by recomputing the attention matrix from the forward pass's per-row
+// log-sum-exp (the recomputation named in "FlashAttention'ı Anlamak Bölüm 1",
+// section 0; the gradient equations are the chain rule of the score and
+// output equations of section 0.2):
+//
+//   P_ij  = exp(scale q_i.k_j - LSE_i)      dV_j = sum_i P_ij dO_i
+//   dP_ij = dO_i . v_j                      D_i  = dO_i . O_i
+//   dS_ij = P_ij (dP_ij - D_i)              dK_j = scale sum_i dS_ij q_i
+//                                           dQ_i = scale sum_j dS_ij k_j
+//
+// Three kernels, no atomics (results do not depend on scheduling):
+//   fa_bwd_delta  D_i from dO and O (one pass over 2 x [rows, 128] bf16).
+//   fa_bwd_dkdv   one workgroup per 128 keys of a head; each wave owns 32
+//                 keys (K and V as MFMA B operands in registers, dK^T and
+//                 dV^T accumulators) and walks the query rows in blocks of
+//                 64: S = Q K^T and dP = dO V^T, P and dS on the VALU,
+//                 dV^T += dO^T P and dK^T += Q^T dS.  The accumulators give
+//                 each lane one key and 16 query rows, so P and dS rounded
+//                 to bf16 are directly the B operands of the next products
+//                 and Q^T / dO^T come from the row-major LDS tiles through
+//                 the transposing read (ds_read_b64_tr_b16).
+//   fa_bwd_dq     one workgroup per 128 query rows (32 per wave), the
+//                 forward's loop shape: S^T = K Q^T and dP^T = V dO^T, then
+//                 dQ^T += K^T dS^T.
+// S and dP are computed in both the dK/dV and the dQ kernel (seven matrix
+// products instead of five) in exchange for no atomic accumulation of dQ.
+// Tiles read both row-wise and transposed use the SWZ_BOTH swizzle.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_kernel.h"
+
+namespace fa06 {
+namespace {
+
+// ---------------------------------------------------------------- delta
+// 16 lanes per row (16 bytes each), 16 rows per 256-thread workgroup,
+// grid-stride over all rows.
+__global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const uint16_t* __restrict__ O,
+                                                           const uint16_t* __restrict__ dO,
+                                                           float* __restrict__ Dl, int64_t rows) {
+  const int part = threadIdx.x & 15;
+  for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); row - (threadIdx.x >> 4) < rows;
+       row += (int64_t)gridDim.x * 16) {
+    float acc = 0.0f;
+    if (row < rows) {
+      const uintx4 o = *reinterpret_cast<const uintx4*>(O + row * D + part * 8);
+      const uintx4 g = *reinterpret_cast<const uintx4*>(dO + row * D + part * 8);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc = __builtin_fmaf(__uint_as_float(o[k] << 16), __uint_as_float(g[k] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(o[k] & 0xFFFF0000u), __uint_as_float(g[k] & 0xFFFF0000u), acc);
+      }
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    if (row < rows && part == 0) Dl[row] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+constexpr int KV_KEYS = 128;  // keys per workgroup (32 per wave)
+constexpr int KV_QB = 64;     // query rows per step
+constexpr int KV_TILE = KV_QB * ROW_BYTES;  // one Q or dO tile: 16 KiB
+// LDS: Q[2], dO[2], LSE[2], D[2]
+constexpr int KV_LDS = 4 * KV_TILE + 4 * KV_QB * 4;
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                   const float* __restrict__ LSE, const float* __restrict__ Dl,
+                   uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+                   int Nq, int Nk, int n_ktiles, float c_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) char smem[KV_LDS];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  const int nfull = nblk & ~7;
+  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+  const int bh = bid / n_ktiles;
+  const int kt = bid - bh * n_ktiles;
+  const int k0 = kt * KV_KEYS;
+  const int kw = k0 + wave * 32;  // this wave's first key
+  const int key = kw + c;         // this lane's key
+
+  const size_t head_q = (size_t)bh * (size_t)Nq;
+  const size_t head_k = (size_t)bh * (size_t)Nk;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + head_q, (uint32_t)Nq * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + head_q, (uint32_t)Nq * 4u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(dK + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(dV + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  // K and V rows of this wave's keys as B operands: kb[t] = K[key][16t + 8h .. +7]
+  // (keys past Nk read as zero; their results are not stored)
+  bf16x8 kb[8], vb[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    kb[t] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
+    vb[t] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
+  }
+
+  // query blocks that see at least one of the workgroup's keys, and the
+  // first block in which every (row, key) pair is visible
+  const int off = Nk - Nq;
+  const int n_qb = (Nq + KV_QB - 1) / KV_QB;
+  int qb_first = 0, qb_unmasked = 0;
+  if constexpr (CAUSAL) {
+    const int first_row = k0 - off;  // first row that sees key k0
+    qb_first = first_row <= 0 ? 0 : first_row / KV_QB;
+    const int last_hidden = k0 + KV_KEYS - 1 - off;  // rows below it miss some key
+    qb_unmasked = last_hidden <= 0 ? 0 : (last_hidden + KV_QB - 1) / KV_QB;
+    qb_first = qb_first < n_qb ? qb_first : n_qb;
+    qb_unmasked = qb_unmasked < qb_first ? qb_first : (qb_unmasked > n_qb ? n_qb : qb_unmasked);
+  }
+
+  char* const qbuf0 = smem;
+  char* const dobuf0 = smem + 2 * KV_TILE;
+  char* const lbuf0 = smem + 4 * KV_TILE;
+  char* const dbuf0 = lbuf0 + 2 * KV_QB * 4;
+  auto stage_in = [&](int qb, int st) FA_INLINE {
+    tile_to_lds<KV_QB, SWZ_BOTH>(rq, (uint32_t)(qb * KV_QB), qbuf0 + st * KV_TILE, wave_u, lane);
+    tile_to_lds<KV_QB, SWZ_BOTH>(rdo, (uint32_t)(qb * KV_QB), dobuf0 + st * KV_TILE, wave_u, lane);
+    // 64 floats of LSE and of D: 16 lanes x 16 bytes each
+    if (wave_u < 2 && lane < 16) {
+      const __amdgpu_buffer_rsrc_t r = wave_u == 0 ? rl : rd;
+      char* dst = (wave_u == 0 ? lbuf0 : dbuf0) + st * KV_QB * 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_char*)dst, 16,
+                                               (uint32_t)lane * 16u,
+                                               __builtin_amdgcn_readfirstlane((uint32_t)(qb * KV_QB * 4)), 0, 0);
+    }
+  };
+
+  floatx16 dvacc[4], dkacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    dvacc[i] = floatx16{};
+    dkacc[i] = floatx16{};
+  }
+
+  // One block of 64 query rows, as two sub-blocks of 32.
+  auto step = [&](int qb, int st, auto mask_tag) FA_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* qs = qbuf0 + st * KV_TILE;
+    const char* ds = dobuf0 + st * KV_TILE;
+    const char* ls = lbuf0 + st * KV_QB * 4;
+    const char* dls = dbuf0 + st * KV_QB * 4;
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0, 0);
+      // accumulator register r holds row ib*32 + 8(r/4) + 4h + r%4 of the block
+      bf16x8 pb[2], dsb[2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + (ib * 32 + 8 * g + 4 * h) * 4);
+        const floatx4 d4 = *reinterpret_cast<const floatx4*>(dls + (ib * 32 + 8 * g + 4 * h) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * LOG2E));
+          if constexpr (MASK) {
+            const int row = qb * KV_QB + ib * 32 + 8 * g + 4 * h + e;
+            if (key > row + off) p = 0.0f;
+          }
+          const float dsv = p * (dp[r] - d4[e]);
+          pb[r >> 3][r & 7] = (__bf16)p;
+          dsb[r >> 3][r & 7] = (__bf16)dsv;
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ds, ib * 32 + ks * 16, cb, lane),
+                                                              pb[ks], dvacc[cb], 0, 0, 0);
+          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(qs, ib * 32 + ks * 16, cb, lane),
+                                                              dsb[ks], dkacc[cb], 0, 0, 0);
+        }
+    }
+  };
+
+  if (qb_first < n_qb) stage_in(qb_first, 0);
+  for (int qb = qb_first; qb < n_qb; ++qb) {
+    const int st = (qb - qb_first) & 1;
+    wait_vmem();
+    __syncthreads();  // stage st landed for every wave; stage st^1 is free
+    if (qb + 1 < n_qb) stage_in(qb + 1, st ^ 1);
+    if (CAUSAL && qb < qb_unmasked)
+      step(qb, st, std::true_type{});
+    else
+      step(qb, st, std::false_type{});
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    store_bf16_row_block(rdk, (uint32_t)key, cb, h, dkacc[cb], scale);
+    store_bf16_row_block(rdv, (uint32_t)key, cb, h, dvacc[cb], 1.0f);
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+constexpr int DQ_ROWS = 128;  // query rows per workgroup (32 per wave)
+constexpr int DQ_BC = 64;     // keys per tile
+constexpr int DQ_TILE = DQ_BC * ROW_BYTES;
+constexpr int DQ_LDS = 4 * DQ_TILE;  // K[2], V[2]
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                 const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+                 const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
+                 int Nq, int Nk, int n_qtiles, float c_log2, float scale) {
+  __shared__ __attribute__((aligned(1024))) char smem[DQ_LDS];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int c = lane & 31;
+  const int h = lane >> 5;
+
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  const int nfull = nblk & ~7;
+  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+  const int bh = bid / n_qtiles;
+  int qt = bid - bh * n_qtiles;
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
+  const int q0 = qt * DQ_ROWS;
+  const int q = q0 + wave * 32 + c;  // this lane's query row
+
+  const size_t head_q = (size_t)bh * (size_t)Nq;
+  const size_t head_k = (size_t)bh * (size_t)Nk;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + head_q, (uint32_t)Nq * 4u);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + head_q, (uint32_t)Nq * 4u);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(dQ + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+
+  const int n_full = Nk / DQ_BC;
+  int n_tiles = n_full + (Nk % DQ_BC != 0);
+  int first_masked = n_full;
+  int key_lim = Nk - 1;
+  if constexpr (CAUSAL) {
+    const int off = Nk - Nq;
+    const int q_last = (q0 + DQ_ROWS < Nq ? q0 + DQ_ROWS : Nq) - 1;
+    const int lim_last = q_last + off;
+    const int lim_first = q0 + off;
+    const int need = lim_last < 0 ? 0 : lim_last / DQ_BC + 1;
+    n_tiles = need < n_tiles ? need : n_tiles;
+    const int unmasked = lim_first + 1 <= 0 ? 0 : (lim_first + 1) / DQ_BC;
+    first_masked = unmasked < first_masked ? unmasked : first_masked;
+    key_lim = q + off < key_lim ? q + off : key_lim;
+  }
+
+  // Q and dO rows of this lane's query as B operands (rows past Nq read 0)
+  bf16x8 qb[8], dob[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    qb[t] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
+    dob[t] = __builtin_bit_cast(bf16x8, buf_load16(rdo, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
+  }
+  const float nl2 = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)q * 4u, 0, 0)) * LOG2E;
+  const float dq_d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)q * 4u, 0, 0));
+
+  floatx16 dqacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dqacc[i] = floatx16{};
+
+  char* const kbuf0 = smem;
+  char* const vbuf0 = smem + 2 * DQ_TILE;
+  auto stage_in = [&](int j, int st) FA_INLINE {
+    tile_to_lds<DQ_BC, SWZ_BOTH>(rk, (uint32_t)(j * DQ_BC), kbuf0 + st * DQ_TILE, wave_u, lane);
+    tile_to_lds<DQ_BC, SWZ_ROW>(rv, (uint32_t)(j * DQ_BC), vbuf0 + st * DQ_TILE, wave_u, lane);
+  };
+
+  // One K/V tile, as two 32-key blocks (short live ranges: S, dP and dS of
+  // one block at a time).
+  auto step = [&](int j, int st, auto mask_tag) FA_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const char* ks = kbuf0 + st * DQ_TILE;
+    const char* vs = vbuf0 + st * DQ_TILE;
+    const int lim = key_lim - j * DQ_BC;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      floatx16 s = floatx16{}, dp = floatx16{};
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
+      // register r holds key kb*32 + 8(r/4) + 4h + r%4 of the tile
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, nl2));
+        if constexpr (MASK) {
+          const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (kk > lim) p = 0.0f;
+        }
+        dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+          dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read_a<SWZ_BOTH>(ks, kb * 32 + k2 * 16, cb, lane), dsb[k2], dqacc[cb], 0, 0, 0);
+    }
+  };
+
+  if (n_tiles > 0) stage_in(0, 0);
+  for (int j = 0; j < n_tiles; ++j) {
+    const int st = j & 1;
+    wait_vmem();
+    __syncthreads();
+    if (j + 1 < n_tiles) stage_in(j + 1, st ^ 1);
+    if (j >= first_masked)
+      step(j, st, std::true_type{});
+    else
+      step(j, st, std::false_type{});
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) store_bf16_row_block(rdq, (uint32_t)q, cb, h, dqacc[cb], scale);
+}
+
+}  // namespace
+
+int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = a.BH * a.Nq;
+  if (rows > 0) {
+    const int64_t want = (rows + 15) / 16;
+    const unsigned grid = (unsigned)(want < (1 << 20) ? want : (1 << 20));
+    const uint16_t* o = static_cast<const uint16_t*>(a.O);
+    const uint16_t* g = static_cast<const uint16_t*>(a.dO);
+    float* dl = a.Dws;
+    int64_t n = rows;
+    void* args[] = {&o, &g, &dl, &n};
+    if (hipLaunchKernel((const void*)&fa_bwd_delta_kernel, dim3(grid), dim3(256), args, 0, stream) != hipSuccess)
+      return 1;
+  }
+  const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
+  const uint16_t* q = static_cast<const uint16_t*>(a.Q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.K);
+  const uint16_t* v = static_cast<const uint16_t*>(a.V);
+  const uint16_t* g = static_cast<const uint16_t*>(a.dO);
+  const float* lse = a.LSE;
+  const float* dl = a.Dws;
+  int nq = (int)a.Nq, nk = (int)a.Nk;
+  float cl = c_log2, sc = a.scale;
+  {
+    int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
+    uint16_t* dk = static_cast<uint16_t*>(a.dK);
+    uint16_t* dv = static_cast<uint16_t*>(a.dV);
+    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc};
+    const void* fn = a.causal ? (const void*)&fa_bwd_dkdv_kernel<true> : (const void*)&fa_bwd_dkdv_kernel<false>;
+    if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
+  }
+  if (rows > 0) {
+    int n_qt = (int)((a.Nq + DQ_ROWS - 1) / DQ_ROWS);
+    uint16_t* dq = static_cast<uint16_t*>(a.dQ);
+    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dq, &nq, &nk, &n_qt, &cl, &sc};
+    const void* fn = a.causal ? (const void*)&fa_bwd_dq_kernel<true> : (const void*)&fa_bwd_dq_kernel<false>;
+    if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
+  }
+  return 0;
+}
+
+const char* bwd_config_string() {
+  return "gfx950 fa_bwd v1: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
+         "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); no atomics";
+}
+
+}  // namespace fa06

@@ -1,0 +1,163 @@
+// fa_device.h -- device helpers shared by the attention kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa06 {
+namespace {
+
+constexpr int D = 128;           // head size (d = d_v)
+constexpr int ROW_BYTES = D * 2; // one bf16 row
+constexpr int NWAVES = 4;
+constexpr int NTHREADS = NWAVES * 64;
+constexpr float LOG2E = 1.44269504088896340736f;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
+typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Buffer resource: base, no stride, num_records bytes; dword3 selects the
+// 32-bit data format, which gfx9-family raw buffer accesses require.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+  return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+}
+
+// LDS tiles hold rows of 256 bytes (sixteen 16-byte chunks); the chunk index
+// is XOR-swizzled per row.  Three swizzles, one per way a tile is read:
+//   SWZ_ROW  chunk ^ (row % 16): 16 lanes reading one chunk of 16
+//            consecutive rows (ds_read_b128 MFMA operands) hit 16 distinct
+//            bank groups.
+//   SWZ_TR   chunk ^ 4*(row % 4): the transposing reads (ds_read_b64_tr_b16)
+//            of 32 lanes cover a 64-byte band of 4 rows; the 4 rows land in
+//            4 distinct bands.
+//   SWZ_BOTH chunk ^ (4*(row % 4) + (row / 4) % 4): both of the above at once
+//            (the high two bits separate the 4 rows of a band, and the map
+//            is one-to-one over 16 rows), for tiles read both ways.
+enum Swz { SWZ_ROW = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
+
+template <int S>
+__device__ inline uint32_t swz_chunk(uint32_t row, uint32_t ch) {
+  if constexpr (S == SWZ_ROW) return ch ^ (row & 15u);
+  else if constexpr (S == SWZ_TR) return ch ^ ((row & 3u) << 2);
+  else return ch ^ (((row & 3u) << 2) | ((row >> 2) & 3u));
+}
+template <int S>
+__device__ inline uint32_t swz(uint32_t row, uint32_t ch) {
+  return row * ROW_BYTES + (swz_chunk<S>(row, ch) << 4);
+}
+__device__ inline uint32_t k_swz(uint32_t row, uint32_t ch) { return swz<SWZ_ROW>(row, ch); }
+__device__ inline uint32_t v_swz(uint32_t row, uint32_t ch) { return swz<SWZ_TR>(row, ch); }
+
+__device__ inline float wave_max_halves(float x) {
+  // lanes l and l^32 hold the same query row
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float wave_min_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ inline float wave_sum_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane L of a wave
+// writes its 16 bytes at lds_base + 16*L, so each instruction fills 1 KiB of
+// LDS linearly.  The swizzle is applied on the source side: the lane that
+// fills physical chunk P of row r loads logical chunk P ^ f(r) (every
+// swizzle is an XOR, its own inverse).  `ROWS` rows starting at global row
+// `row0` (scalar) go to `lds`; every wave issues ROWS*16/64/NWAVES
+// instructions.
+template <int ROWS, int S>
+__device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * ROW_BYTES);
+  constexpr int N_INST = ROWS * 16 / 64 / NWAVES;
+  static_assert(N_INST >= 1, "tile too small for one copy per wave");
+#pragma unroll
+  for (int i = 0; i < N_INST; ++i) {
+    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block (4 rows)
+    const uint32_t row = blk * 4 + ((uint32_t)lane >> 4);
+    const uint32_t pos = (uint32_t)lane & 15u;                // physical chunk in the row
+    const uint32_t ch = swz_chunk<S>(row, pos);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)((lds_char*)lds + blk * 1024u), 16,
+        row * ROW_BYTES + (ch << 4), soff, 0, 0);
+  }
+}
+
+// Every helper lambda of a kernel is inlined: loop bodies must stay one
+// straight-line region with all state in registers.
+#define FA_INLINE __attribute__((always_inline))
+
+// Wait until this wave's outstanding global loads (incl. LDS-direct) landed.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Keeps a value live at this point, so the instructions that produce it stay
+// ahead of it (in the same basic block) instead of being sunk into a later
+// block by the compiler.
+__device__ inline void keep(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(uintx4, x))); }
+__device__ inline void keep(float x) { asm volatile("" ::"v"(x)); }
+
+// Transposing LDS read of an MFMA A operand: lane (16-lane group g, i16)
+// gets 8 bf16 of column block `cb` (32 columns) at rows r0 and r0 + 8 of
+// `tile`, where r0 = row_base + 4*(g/2) + (i16/4).  Rows are the k index in
+// the order the 32x32 accumulator holds them (rows 4h..4h+3 and 8+4h..8+4h+3
+// of each 16), so an accumulator turned into bf16 is the matching B operand.
+template <int S>
+__device__ inline bf16x8 tr_read_a(const char* tile, uint32_t row_base, int cb, int lane) {
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  const int sub = i16 >> 2;
+  const int q4 = i16 & 3;
+  const int hh = g >> 1;
+  const int d0 = cb * 32 + (g & 1) * 16 + q4 * 4;
+  const uint32_t ch = (uint32_t)d0 >> 3;
+  const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
+  const uint32_t r0 = row_base + 4 * hh + sub;
+  const uint32_t r1 = r0 + 8;
+  const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S>(r0, ch) + within));
+  const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S>(r1, ch) + within));
+  // move the two 4-element results as whole dwords: a = {lo[0..3], hi[0..3]}
+  const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
+  const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
+  return __builtin_bit_cast(bf16x8, uintx4{lo2.x, lo2.y, hi2.x, hi2.y});
+}
+
+// Row read of an MFMA A operand: lane (c, h) gets chunk 2t+h of row
+// row_base + c (8 bf16 along the contraction index).
+template <int S>
+__device__ inline bf16x8 row_read_a(const char* tile, uint32_t row_base, int t, int c, int h) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(tile + swz<S>(row_base + c, 2 * t + h)));
+}
+
+// Stores a 32x32 fp32 accumulator block holding (column block cb, 32 rows
+// of 4-row groups) as bf16: lane (c, h) writes row `row` (its column c of
+// the transposed accumulator), columns cb*32 + 8*g4 + 4h .. +3.
+__device__ inline void store_bf16_row_block(__amdgpu_buffer_rsrc_t r, uint32_t row, int cb, int h,
+                                            const floatx16& acc, float mul) {
+#pragma unroll
+  for (int g4 = 0; g4 < 4; ++g4) {
+    const int d = cb * 32 + g4 * 8 + 4 * h;
+    const __bf16 a0 = (__bf16)(acc[4 * g4 + 0] * mul);
+    const __bf16 a1 = (__bf16)(acc[4 * g4 + 1] * mul);
+    const __bf16 a2 = (__bf16)(acc[4 * g4 + 2] * mul);
+    const __bf16 a3 = (__bf16)(acc[4 * g4 + 3] * mul);
+    const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+    const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16);
+    __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, r, row * ROW_BYTES + d * 2, 0, 0);
+  }
+}
+
+}  // namespace
+}  // namespace fa06

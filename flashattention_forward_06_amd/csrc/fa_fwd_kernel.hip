@@ -57,101 +57,18 @@
 
 #include <type_traits>
 
+#include "fa_device.h"
 #include "fa_kernel.h"
 
 namespace fa06 {
 namespace {
 
-constexpr int D = 128;          // head size (d = d_v)
-constexpr int ROW_BYTES = D * 2; // one bf16 row
 constexpr int BR = 128;         // query rows per workgroup
-constexpr int NWAVES = 4;
-constexpr int NTHREADS = NWAVES * 64;
 constexpr int Q_BYTES = BR * ROW_BYTES;      // the Q tile, staged once: 32 KiB
 // K and V tiles of BC keys, two of each in LDS (K(j+2), K(j+3), V(j), V(j+1)):
 // 64 KiB at BC = 64, which leaves room for two workgroups per CU.
 constexpr int lds_bytes(int bc) { return 4 * bc * ROW_BYTES > Q_BYTES ? 4 * bc * ROW_BYTES : Q_BYTES; }
 constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
-typedef unsigned uintx2 __attribute__((ext_vector_type(2)));
-typedef unsigned uintx4 __attribute__((ext_vector_type(4)));
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// Buffer resource: base, no stride, num_records bytes; dword3 selects the
-// 32-bit data format, which gfx9-family raw buffer accesses require.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-__device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
-  return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
-}
-
-// Swizzled byte offset of 16-byte chunk `ch` of row `row` in a K or Q tile:
-// any 16 consecutive rows place a given chunk in 16 distinct bank groups.
-__device__ inline uint32_t k_swz(uint32_t row, uint32_t ch) {
-  return row * ROW_BYTES + ((ch ^ (row & 15u)) << 4);
-}
-// V tile: the transposing reads touch a 64-byte band (4 chunks) of 8 rows at
-// once; XOR-ing the band index with row%4 spreads 4 rows over the 256 bytes.
-__device__ inline uint32_t v_swz(uint32_t row, uint32_t ch) {
-  return row * ROW_BYTES + ((ch ^ ((row & 3u) << 2)) << 4);
-}
-
-__device__ inline float wave_max_halves(float x) {
-  // lanes l and l^32 hold the same query row
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ inline float wave_min_halves(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fminf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-__device__ inline float wave_sum_halves(float x) {
-  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
-}
-
-// Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane L of a wave
-// writes its 16 bytes at lds_base + 16*L, so each instruction fills 1 KiB of
-// LDS linearly.  The swizzle is applied on the source side: the lane that
-// fills physical chunk P of row r loads logical chunk P ^ f(r).
-// `rows` rows starting at global row `row0` (scalar) go to `lds`; every wave
-// issues rows*16/64/NWAVES instructions.
-template <int ROWS, bool IS_V>
-__device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
-  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * ROW_BYTES);
-  constexpr int N_INST = ROWS * 16 / 64 / NWAVES;
-#pragma unroll
-  for (int i = 0; i < N_INST; ++i) {
-    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block (4 rows)
-    const uint32_t row = blk * 4 + ((uint32_t)lane >> 4);
-    const uint32_t pos = (uint32_t)lane & 15u;                // physical chunk in the row
-    const uint32_t ch = IS_V ? (pos ^ ((row & 3u) << 2)) : (pos ^ (row & 15u));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)((lds_char*)lds + blk * 1024u), 16,
-        row * ROW_BYTES + (ch << 4), soff, 0, 0);
-  }
-}
-
-// Every helper lambda of the kernel is inlined: the loop body must stay one
-// straight-line region with all state in registers.
-#define FA_INLINE __attribute__((always_inline))
-
-// Wait until this wave's outstanding global loads (incl. LDS-direct) landed.
-__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Keeps a value live at this point, so the instructions that produce it stay
-// ahead of it (in the same basic block) instead of being sunk into a later
-// block by the compiler.
-__device__ inline void keep(const bf16x8& x) { asm volatile("" ::"v"(__builtin_bit_cast(uintx4, x))); }
-__device__ inline void keep(float x) { asm volatile("" ::"v"(x)); }
-
-constexpr float LOG2E = 1.44269504088896340736f;
 
 // One workgroup computes BR query rows of one (batch, head) against all keys.
 //   BC        keys per K/V tile (64; 32 for the bias variant, whose bias
@@ -260,7 +177,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * TILE_BYTES; };
 
   // ---- prologue: the Q tile through LDS into registers.
-  tile_to_lds<BR, false>(rq, q0, smem, wave_u, lane);
+  tile_to_lds<BR, SWZ_ROW>(rq, q0, smem, wave_u, lane);
   wait_vmem();
   __syncthreads();
   bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
@@ -271,9 +188,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + k_swz(row, 2 * t + h)));
   }
   __syncthreads();  // the Q staging area is reused from here on
-  tile_to_lds<BC, false>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, false>(rk, BC, kbuf(1), wave_u, lane);
-  tile_to_lds<BC, true>(rv, 0, vbuf(0), wave_u, lane);
+  tile_to_lds<BC, SWZ_ROW>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW>(rk, BC, kbuf(1), wave_u, lane);
+  tile_to_lds<BC, SWZ_TR>(rv, 0, vbuf(0), wave_u, lane);
   floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
   if constexpr (BIAS) {
     load_bias(0, b0);
@@ -368,7 +285,13 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float x = BIAS ? s[kb][r] - m_use : __builtin_fmaf(s[kb][r], c_log2, -m_use);
-        const float p = __builtin_amdgcn_exp2f(x);
+        float p = __builtin_amdgcn_exp2f(x);
+        if constexpr (MASK && !BIAS) {
+          // a hidden key's score is +-inf, and inf * scale is NaN when the
+          // scale is 0: zero it explicitly
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key > lim) p = 0.0f;
+        }
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
@@ -428,7 +351,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles > 1) scores(kbuf(1), s1);
   }
   __syncthreads();  // K(0) consumed: K(2) goes into its buffer
-  if (n_tiles > 2) tile_to_lds<BC, false>(rk, 2 * BC, kbuf(0), wave_u, lane);
+  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW>(rk, 2 * BC, kbuf(0), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
@@ -446,8 +369,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
     constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
-    if (j + 3 < n_tiles) tile_to_lds<BC, false>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_S1) tile_to_lds<BC, true>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
     if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
     floatx16 s2[KB];
     if constexpr (HAS_S2) scores(kbuf(P), s2);

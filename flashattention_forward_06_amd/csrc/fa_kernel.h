@@ -23,4 +23,25 @@ struct LaunchArgs {
 int launch_fa_fwd(const LaunchArgs& args, hipStream_t stream);
 const char* kernel_config_string();
 
+// One backward call over BH = B*H heads, already validated.
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* LSE;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dws;           // [BH, Nq] fp32: receives D_i = dO_i . O_i
+  int64_t BH, Nq, Nk;
+  float scale;
+  bool causal;
+};
+
+// Enqueues the three backward kernels; returns 0 or non-zero if a launch failed.
+int launch_fa_bwd(const BwdArgs& args, hipStream_t stream);
+const char* bwd_config_string();
+
 }  // namespace fa06

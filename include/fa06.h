@@ -119,11 +119,46 @@ int fa_fwd_masked(const void *Q, const void *K, const void *V, void *O, float *L
                   int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
                   int64_t bias_stride_q, void *stream);
 
+/*
+ * fa_bwd -- gradients of a scalar loss L through the attention output, given
+ * dO = dL/dO, by recomputing the attention matrix from the forward pass's
+ * log-sum-exp (the recomputation of "FlashAttention'ı Anlamak Bölüm 1",
+ * section 0; the gradients are the chain rule of the score and output
+ * equations of section 0.2).  Per head and query row i:
+ *     P_ij = exp(scale q_i.k_j - LSE_i) (0 for keys hidden by the causal mask),
+ *     dV_j = sum_i P_ij dO_i,  dP_ij = dO_i . v_j,  D_i = dO_i . O_i,
+ *     dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale sum_j dS_ij k_j,
+ *     dK_j = scale sum_i dS_ij q_i.
+ *
+ *   Q, K, V  device, bf16 [B, H, Nq|Nk, d], the forward pass's inputs.
+ *   O, LSE   device, the forward pass's outputs for the same inputs, scale
+ *            and causal flag (bf16 [B, H, Nq, d]; fp32 [B, H, Nq]).
+ *   dO       device, bf16 [B, H, Nq, d].
+ *   dQ, dK, dV  device, bf16 outputs shaped like Q, K, V (written, not
+ *            accumulated into).
+ *   D        device, fp32 [B, H, Nq] workspace owned by the caller; receives
+ *            D_i = dO_i . O_i.
+ *   B, H, Nq, Nk, d, scale, causal, stream  as for fa_fwd_masked (no bias).
+ *
+ * Requirements and errors as for fa_fwd; every pointer must be 16-byte
+ * aligned except LSE and D (4 bytes); an output (dQ, dK, dV, D) that overlaps
+ * an input or another output returns FA_ERR_ALIAS.  B*H == 0 is a no-op; with
+ * Nq == 0, dK and dV are written as zeros.  The call enqueues three kernels
+ * on `stream` and is deterministic (no atomics).
+ */
+int fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+           const float *LSE, void *dQ, void *dK, void *dV, float *D,
+           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+           int causal, void *stream);
+
 /* fa_status_string -- static, NUL-terminated description of a status code. */
 const char *fa_status_string(int status);
 
-/* fa_build_info -- static string naming the kernel's tile configuration. */
+/* fa_build_info -- static string naming the forward kernel's tile configuration. */
 const char *fa_build_info(void);
+
+/* fa_bwd_build_info -- static string naming the backward kernels' configuration. */
+const char *fa_bwd_build_info(void);
 
 #ifdef __cplusplus
 }

@@ -21,7 +21,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_fwd", "fa_fwd_masked", "fa_status_string"]
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_masked", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
 
@@ -137,3 +137,37 @@ def test_python_wrapper_type_checks():
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         fa.load_library(str(tmp_path / "nope.so"))
+
+
+# backward: fake buffers for O, dO, dQ, dK, dV and D
+Op2, dOp = 0x70000000, 0x80000000
+dQp, dKp, dVp, Dp = 0x90000000, 0xA0000000, 0xB0000000, 0xC0000000
+GOOD_BWD = dict(q=Qp, k=Kp, v=Vp, o=Op2, do=dOp, lse=Lp, dq=dQp, dk=dKp, dv=dVp, dl=Dp,
+                B=1, H=2, Nq=256, Nk=256, d=128, scale=0.088, causal=0)
+
+
+def call_bwd(**kw):
+    a = {**GOOD_BWD, **kw}
+    return fa.fa_bwd_raw(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["dl"],
+                         a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dl=0), 1),
+    (dict(B=-1), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2),
+    (dict(d=64), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(o=Op2 + 8), 3), (dict(dv=dVp + 4), 3), (dict(dl=Dp + 2), 3),
+    (dict(dq=Qp), 4), (dict(dk=Kp + 256), 4), (dict(dv=dKp), 4), (dict(dl=Lp), 4), (dict(dq=dOp + 512), 4),
+    (dict(scale=float("nan")), 5),
+    (dict(B=0), 0),
+])
+def test_bwd_validation_codes(kw, code):
+    assert call_bwd(**kw) == code
+
+
+def test_bwd_accepted_arguments_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch on fake pointers")
+    assert call_bwd() == 6
+    assert call_bwd(Nq=0) == 6     # dK and dV must still be zeroed on the device

@@ -67,6 +67,18 @@ def test_scale_variants(fa, scale, note):
     check_parity(Og, Lg, Oo, Lo, note)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_with_masked_tiles(fa, causal):
+    # hidden keys carry -inf scores; with scale 0 they must still weigh 0
+    import torch
+    say(f"case zero scale, ragged keys, causal={causal}")
+    Q, K, V = fi.make_qkv(1, 2, 190, 260, 128, seed=41)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=0.0, causal=causal)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attention_masked(Q, K, V, 0.0, causal=causal)
+    check_parity(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Oo, Lo, f"zero scale causal={causal}")
+
+
 def test_large_logits_and_max_jumps(fa):
     # same value recipe as the 16K workload, at a size the oracle finishes in seconds
     say("case koffset small: K*4, 1% rows +8, B=1 H=2 Nq=256 Nk=2048")
