@@ -63,6 +63,10 @@ def parse():
                         "[1, H, Nq, Nk] (read from HBM every call), 'keys' = one random value per "
                         "(b, h, key), broadcast over the rows ([B, H, 1, Nk]).  Without a bias the "
                         "oracle sample is timed; with one it is skipped")
+    p.add_argument("--bwd", action="store_true",
+                   help="time the backward pass (fa_bwd: dQ, dK, dV from dO, with O and LSE from one forward "
+                        "call) instead of the forward; FLOP = 2.5x the forward's (five matrix products; the "
+                        "kernels' recomputation of S and dP in the dQ pass is not counted)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of attention, run a plain copy kernel (256 MiB read + 256 MiB "
@@ -200,6 +204,23 @@ def main():
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
     flop = 4 * w.B * w.H * w.d * visible_pairs(w.Nq, w.Nk, args.causal)
+    if args.bwd:
+        if bias is not None:
+            raise SystemExit("--bwd takes no bias")
+        dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d, seed=w.seed + 5000)[0]
+        g = up(dO)
+        rc = call(*call_args)  # forward once: O and LSE
+        if rc != 0:
+            raise fa.FaError(rc, fa.fa_status_string(rc))
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dv = torch.empty_like(v)
+        delta = torch.empty_like(lse)
+        call = fa.fa_bwd_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), sptr)
+        flop = flop * 5 // 2
 
     def step():
         rc = call(*call_args)
@@ -232,12 +253,12 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
         "traffic": (MEASURED_TRAFFIC["bytes"]
-                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal
+                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
                         and bias is None and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
     }
     out = {
-        "metric": "fwd attention TFLOP/s (bf16, d=128, non-causal) and % of MI355X MFMA peak",
+        "metric": ("bwd" if args.bwd else "fwd") + " attention TFLOP/s (bf16, d=128, non-causal) and % of MI355X MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -250,17 +271,19 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + ("+causal" if args.causal else "") +
-                   ("" if bias is None else f"+bias_{args.bias}"), "B": w.B, "H": w.H,
+                   ("" if bias is None else f"+bias_{args.bias}") + ("+bwd" if args.bwd else ""), "B": w.B, "H": w.H,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": bool(args.causal), "bias": args.bias,
                    "flop_per_step": flop, "scale": w.scale, "seed": w.seed,
                    "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-                   "kernel": fa.fa_build_info()},
+                   "kernel": fa.fa_bwd_build_info() if args.bwd else fa.fa_build_info()},
         "roofline": roof,
         "cpu_baseline": None,
     }
     if bias is not None:
         out["bias_bytes"] = bias.numel() * 4
-    if not args.no_cpu_baseline and bias is None:
+    if args.bwd:
+        out["roofline"]["note"] = "whole backward call (delta + dK/dV + dQ kernels); per-kernel split in profiles/"
+    if not args.no_cpu_baseline and bias is None and not args.bwd:
         cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse, causal=args.causal)
         out["cpu_baseline"] = cb
         out["parity_sampled"] = parity
