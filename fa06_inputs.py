@@ -77,10 +77,10 @@ class Workload:
         return s
 
 
-# The five workloads: a tiny case, the RTX 5090 benchmark shape
-# (bs=1, heads=8, q=4096, kv=8192), and 16K tokens at 4K/8K/16K sequence
-# length with 16 heads; the last one stresses large logits and running-max
-# jumps.
+# The workloads: a tiny case, the RTX 5090 benchmark shape (bs=1, heads=8,
+# q=4096, kv=8192), and 16K tokens at 4K/8K/16K sequence length with 16
+# heads of size 128 (the 16K one stresses large logits and running-max
+# jumps); then head sizes 64 and 256 at 8K.
 WORKLOADS = {
     "tiny_256": Workload("tiny_256", 1, 1, 256, 256, seed=1001),
     "rtx5090_q4096_kv8192": Workload("rtx5090_q4096_kv8192", 1, 8, 4096, 8192, seed=1002),
@@ -89,6 +89,9 @@ WORKLOADS = {
     "b1_h16_n16384_koffset": Workload(
         "b1_h16_n16384_koffset", 1, 16, 16384, 16384, seed=1005,
         k_scale=4.0, offset_frac=0.01, offset=8.0),
+    # other head sizes at the same hidden size H*d = 2048 and 16K tokens
+    "b2_h32_n8192_d64": Workload("b2_h32_n8192_d64", 2, 32, 8192, 8192, d=64, seed=1006),
+    "b2_h8_n8192_d256": Workload("b2_h8_n8192_d256", 2, 8, 8192, 8192, d=256, seed=1007),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 

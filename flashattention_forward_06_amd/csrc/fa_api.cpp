@@ -38,6 +38,10 @@ int check_device() {
   return s == 1 ? FA_OK : FA_ERR_DEVICE;
 }
 
+// Longest sequence for head size d: one (batch, head) slice of N rows of 2d
+// bytes stays within 2^31 bytes (32-bit buffer offsets), and N <= 2^23.
+int64_t max_seq(int64_t d) { return (int64_t(1) << 30) / d < FA_MAX_SEQ ? (int64_t(1) << 30) / d : FA_MAX_SEQ; }
+
 }  // namespace
 
 namespace {
@@ -52,14 +56,14 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
                         int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
                         int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
-  if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
-  if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (Nq > max_seq(d) || Nk > max_seq(d)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
-  // sizes: B*H*N*d*2 bytes must fit in int64 (N <= 2^23, d*2 = 2^8)
+  // sizes: B*H*N*d*2 bytes must fit in int64 (N*d*2 <= 2^31)
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
-  const int64_t row_bytes = FA_HEAD_DIM * 2;
-  if (BH > (INT64_MAX / row_bytes) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
+  const int64_t row_bytes = d * 2;
+  if (BH > (INT64_MAX / row_bytes) / max_seq(d)) return FA_ERR_INVALID_SHAPE;
   // bias: non-negative element strides; the extent must be addressable
   int64_t bias_elems = 0;
   if (bias != nullptr) {
@@ -102,6 +106,7 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
   a.H = H;
   a.Nq = Nq;
   a.Nk = Nk;
+  a.d = d;
   a.scale = scale;
   a.causal = causal == 1;
   a.bias = bias;
@@ -189,7 +194,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a pointer to a non-empty buffer is NULL";
     case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: B, H, Nq must be >= 0, Nk >= 1, and sizes must fit";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 128, N <= 2^23, pointers 16-byte aligned (LSE 4), "
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64, 128 or 256 (128 for fa_bwd), N <= min(2^23, 2^30/d), "
+                                     "pointers 16-byte aligned (LSE 4), "
                                      "bias strides non-negative multiples of 4 within the addressable span";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: O or LSE overlaps Q, K, V or each other";
     case FA_ERR_INVALID_SCALE: return "FA_ERR_INVALID_SCALE: scale must be finite";

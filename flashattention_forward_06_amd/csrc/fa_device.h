@@ -30,28 +30,33 @@ __device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint
   return __builtin_bit_cast(uintx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }
 
-// LDS tiles hold rows of 256 bytes (sixteen 16-byte chunks); the chunk index
-// is XOR-swizzled per row.  Three swizzles, one per way a tile is read:
-//   SWZ_ROW  chunk ^ (row % 16): 16 lanes reading one chunk of 16
-//            consecutive rows (ds_read_b128 MFMA operands) hit 16 distinct
-//            bank groups.
-//   SWZ_TR   chunk ^ 4*(row % 4): the transposing reads (ds_read_b64_tr_b16)
-//            of 32 lanes cover a 64-byte band of 4 rows; the 4 rows land in
-//            4 distinct bands.
-//   SWZ_BOTH chunk ^ (4*(row % 4) + (row / 4) % 4): both of the above at once
-//            (the high two bits separate the 4 rows of a band, and the map
-//            is one-to-one over 16 rows), for tiles read both ways.
+// LDS tiles hold rows of 2*DIM bytes (DIM/8 chunks of 16 bytes); the chunk
+// index is XOR-swizzled per row.  Three swizzles, one per way a tile is read:
+//   SWZ_ROW  16 lanes reading one chunk of 16 consecutive rows (ds_read_b128
+//            MFMA operands) hit 16 distinct 16-byte bank groups.
+//   SWZ_TR   the transposing reads (ds_read_b64_tr_b16) of 32 lanes cover
+//            a 64-byte band of 4 rows; the 4 rows land in distinct groups.
+//   SWZ_BOTH both at once, for tiles read both ways.
+// With 256- or 512-byte rows every row starts at the same bank, so the XOR
+// must separate rows: ROW uses chunk ^ (row % 16), TR chunk ^ 4*(row % 4),
+// BOTH chunk ^ (4*(row % 4) + (row / 4) % 4) (the high two bits separate the
+// 4 rows of a band, and the map is one-to-one over 16 rows).  With 128-byte
+// rows (DIM = 64) odd rows start half way round the banks, so row pairs
+// already differ; the XOR acts on row / 2: chunk ^ (4*((row/2) % 2) +
+// (row/4) % 4), which serves both access patterns.
 enum Swz { SWZ_ROW = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
 
-template <int S>
+template <int S, int DIM = D>
 __device__ inline uint32_t swz_chunk(uint32_t row, uint32_t ch) {
-  if constexpr (S == SWZ_ROW) return ch ^ (row & 15u);
+  static_assert(DIM == 64 || DIM == 128 || DIM == 256, "head size");
+  if constexpr (DIM == 64) return ch ^ ((((row >> 1) & 1u) << 2) | ((row >> 2) & 3u));
+  else if constexpr (S == SWZ_ROW) return ch ^ (row & 15u);
   else if constexpr (S == SWZ_TR) return ch ^ ((row & 3u) << 2);
   else return ch ^ (((row & 3u) << 2) | ((row >> 2) & 3u));
 }
-template <int S>
+template <int S, int DIM = D>
 __device__ inline uint32_t swz(uint32_t row, uint32_t ch) {
-  return row * ROW_BYTES + (swz_chunk<S>(row, ch) << 4);
+  return row * (uint32_t)(2 * DIM) + (swz_chunk<S, DIM>(row, ch) << 4);
 }
 __device__ inline uint32_t k_swz(uint32_t row, uint32_t ch) { return swz<SWZ_ROW>(row, ch); }
 __device__ inline uint32_t v_swz(uint32_t row, uint32_t ch) { return swz<SWZ_TR>(row, ch); }
@@ -72,25 +77,29 @@ __device__ inline float wave_sum_halves(float x) {
 
 // Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane L of a wave
 // writes its 16 bytes at lds_base + 16*L, so each instruction fills 1 KiB of
-// LDS linearly.  The swizzle is applied on the source side: the lane that
-// fills physical chunk P of row r loads logical chunk P ^ f(r) (every
-// swizzle is an XOR, its own inverse).  `ROWS` rows starting at global row
-// `row0` (scalar) go to `lds`; every wave issues ROWS*16/64/NWAVES
-// instructions.
-template <int ROWS, int S>
+// LDS linearly (1024 / (2*DIM) rows).  The swizzle is applied on the source
+// side: the lane that fills physical chunk P of row r loads logical chunk
+// P ^ f(r) (every swizzle is an XOR, its own inverse).  `ROWS` rows starting
+// at global row `row0` (scalar) go to `lds`; every wave issues
+// ROWS*2*DIM/1024/NWAVES instructions.
+template <int ROWS, int S, int DIM = D>
 __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
-  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * ROW_BYTES);
-  constexpr int N_INST = ROWS * 16 / 64 / NWAVES;
+  constexpr uint32_t RB = 2 * DIM;          // bytes per row
+  constexpr uint32_t CH = DIM / 8;          // chunks per row
+  constexpr uint32_t RPK = 1024 / RB;       // rows per 1 KiB block
+  constexpr uint32_t CH_SHIFT = DIM == 64 ? 3 : (DIM == 128 ? 4 : 5);
+  const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * RB);
+  constexpr int N_INST = ROWS * (int)RB / 1024 / NWAVES;
   static_assert(N_INST >= 1, "tile too small for one copy per wave");
 #pragma unroll
   for (int i = 0; i < N_INST; ++i) {
-    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block (4 rows)
-    const uint32_t row = blk * 4 + ((uint32_t)lane >> 4);
-    const uint32_t pos = (uint32_t)lane & 15u;                // physical chunk in the row
-    const uint32_t ch = swz_chunk<S>(row, pos);
+    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block
+    const uint32_t row = blk * RPK + ((uint32_t)lane >> CH_SHIFT);
+    const uint32_t pos = (uint32_t)lane & (CH - 1u);          // physical chunk in the row
+    const uint32_t ch = swz_chunk<S, DIM>(row, pos);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)((lds_char*)lds + blk * 1024u), 16,
-        row * ROW_BYTES + (ch << 4), soff, 0, 0);
+        row * RB + (ch << 4), soff, 0, 0);
   }
 }
 
@@ -112,7 +121,7 @@ __device__ inline void keep(float x) { asm volatile("" ::"v"(x)); }
 // `tile`, where r0 = row_base + 4*(g/2) + (i16/4).  Rows are the k index in
 // the order the 32x32 accumulator holds them (rows 4h..4h+3 and 8+4h..8+4h+3
 // of each 16), so an accumulator turned into bf16 is the matching B operand.
-template <int S>
+template <int S, int DIM = D>
 __device__ inline bf16x8 tr_read_a(const char* tile, uint32_t row_base, int cb, int lane) {
   const int g = lane >> 4;
   const int i16 = lane & 15;
@@ -125,9 +134,9 @@ __device__ inline bf16x8 tr_read_a(const char* tile, uint32_t row_base, int cb, 
   const uint32_t r0 = row_base + 4 * hh + sub;
   const uint32_t r1 = r0 + 8;
   const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S>(r0, ch) + within));
+      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S, DIM>(r0, ch) + within));
   const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S>(r1, ch) + within));
+      (__attribute__((address_space(3))) shortx4*)((lds_char*)tile + swz<S, DIM>(r1, ch) + within));
   // move the two 4-element results as whole dwords: a = {lo[0..3], hi[0..3]}
   const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
   const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
@@ -136,14 +145,15 @@ __device__ inline bf16x8 tr_read_a(const char* tile, uint32_t row_base, int cb, 
 
 // Row read of an MFMA A operand: lane (c, h) gets chunk 2t+h of row
 // row_base + c (8 bf16 along the contraction index).
-template <int S>
+template <int S, int DIM = D>
 __device__ inline bf16x8 row_read_a(const char* tile, uint32_t row_base, int t, int c, int h) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(tile + swz<S>(row_base + c, 2 * t + h)));
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(tile + swz<S, DIM>(row_base + c, 2 * t + h)));
 }
 
 // Stores a 32x32 fp32 accumulator block holding (column block cb, 32 rows
 // of 4-row groups) as bf16: lane (c, h) writes row `row` (its column c of
 // the transposed accumulator), columns cb*32 + 8*g4 + 4h .. +3.
+template <int DIM = D>
 __device__ inline void store_bf16_row_block(__amdgpu_buffer_rsrc_t r, uint32_t row, int cb, int h,
                                             const floatx16& acc, float mul) {
 #pragma unroll
@@ -155,7 +165,7 @@ __device__ inline void store_bf16_row_block(__amdgpu_buffer_rsrc_t r, uint32_t r
     const __bf16 a3 = (__bf16)(acc[4 * g4 + 3] * mul);
     const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
     const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16);
-    __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, r, row * ROW_BYTES + d * 2, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, r, row * (uint32_t)(2 * DIM) + d * 2, 0, 0);
   }
 }
 

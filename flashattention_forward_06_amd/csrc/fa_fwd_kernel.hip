@@ -64,10 +64,15 @@ namespace fa06 {
 namespace {
 
 constexpr int BR = 128;         // query rows per workgroup
-constexpr int Q_BYTES = BR * ROW_BYTES;      // the Q tile, staged once: 32 KiB
-// K and V tiles of BC keys, two of each in LDS (K(j+2), K(j+3), V(j), V(j+1)):
-// 64 KiB at BC = 64, which leaves room for two workgroups per CU.
-constexpr int lds_bytes(int bc) { return 4 * bc * ROW_BYTES > Q_BYTES ? 4 * bc * ROW_BYTES : Q_BYTES; }
+// LDS: the Q tile (BR rows, staged once) and K and V tiles of BC keys, two of
+// each (K(j+2), K(j+3), V(j), V(j+1)): 64 KiB at head size 128 and BC = 64,
+// which leaves room for two workgroups per CU.
+constexpr int lds_bytes(int bc, int dim) {
+  return 4 * bc * 2 * dim > BR * 2 * dim ? 4 * bc * 2 * dim : BR * 2 * dim;
+}
+// Waves per SIMD the register budget allows: head size 256 keeps a 32x256
+// fp32 output accumulator (128 registers) per wave and runs one wave.
+constexpr int waves_per_simd(int dim) { return dim == 256 ? 1 : 2; }
 constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 
 // One workgroup computes BR query rows of one (batch, head) against all keys.
@@ -78,16 +83,19 @@ constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 //             a q-tile's diagonal are skipped, tiles crossing it are masked
 //   BIAS      an fp32 bias is added to the scaled scores:
 //             bias[b*sb + h*sh + i*sq + j] (element strides)
-template <int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+template <int DIM, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(DIM), waves_per_simd(DIM))))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
               const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H,
               int Nq, int Nk, int n_qtiles, float c_log2) {
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
-  constexpr int TILE_BYTES = BC * ROW_BYTES;  // one K or V tile
-  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC)];
+  constexpr int RB = 2 * DIM;                 // bytes per row
+  constexpr int NT = DIM / 16;                // 16-wide k steps over the head size
+  constexpr int NCB = DIM / 32;               // 32-column blocks of the output
+  constexpr int TILE_BYTES = BC * RB;         // one K or V tile
+  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC, DIM)];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -105,12 +113,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
 
-  const size_t head_q = (size_t)bh * (size_t)Nq * D;
-  const size_t head_k = (size_t)bh * (size_t)Nk * D;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q, (uint32_t)Nq * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * ROW_BYTES);
+  const size_t head_q = (size_t)bh * (size_t)Nq * DIM;
+  const size_t head_k = (size_t)bh * (size_t)Nk * DIM;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q, (uint32_t)Nq * RB);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k, (uint32_t)Nk * RB);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k, (uint32_t)Nk * RB);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * RB);
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n_full = Nk / BC;  // tiles with BC valid keys
@@ -133,9 +141,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // no row of this q-tile sees any key: O = 0, LSE = -inf
       const int q = q0 + wave * 32 + c;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)  // this lane's half row: bytes [128h, 128h + 128)
+      for (int i = 0; i < DIM / 16; ++i)  // this lane's half row: bytes [DIM*h, DIM*h + DIM)
         __builtin_amdgcn_raw_buffer_store_b128(uintx4{0u, 0u, 0u, 0u}, ro,
-                                               (uint32_t)q * ROW_BYTES + 128u * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
+                                               (uint32_t)q * RB + (uint32_t)DIM * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
       if (h == 0 && q < Nq) LSE[(size_t)bh * Nq + q] = -__builtin_inff();
       return;
     }
@@ -177,20 +185,20 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * TILE_BYTES; };
 
   // ---- prologue: the Q tile through LDS into registers.
-  tile_to_lds<BR, SWZ_ROW>(rq, q0, smem, wave_u, lane);
+  tile_to_lds<BR, SWZ_ROW, DIM>(rq, q0, smem, wave_u, lane);
   wait_vmem();
   __syncthreads();
-  bf16x8 qb[8];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
+  bf16x8 qb[NT];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
   {
     const uint32_t row = wave * 32 + c;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + k_swz(row, 2 * t + h)));
+    for (int t = 0; t < NT; ++t)
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + swz<SWZ_ROW, DIM>(row, 2 * t + h)));
   }
   __syncthreads();  // the Q staging area is reused from here on
-  tile_to_lds<BC, SWZ_ROW>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW>(rk, BC, kbuf(1), wave_u, lane);
-  tile_to_lds<BC, SWZ_TR>(rv, 0, vbuf(0), wave_u, lane);
+  tile_to_lds<BC, SWZ_ROW, DIM>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DIM>(rk, BC, kbuf(1), wave_u, lane);
+  tile_to_lds<BC, SWZ_TR, DIM>(rv, 0, vbuf(0), wave_u, lane);
   floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
   if constexpr (BIAS) {
     load_bias(0, b0);
@@ -199,9 +207,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   wait_vmem();
   __syncthreads();
 
-  floatx16 oacc[4];
+  floatx16 oacc[NCB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) oacc[i] = floatx16{};
+  for (int i = 0; i < NCB; ++i) oacc[i] = floatx16{};
   float m_run = -__builtin_inff();  // running max, log2 units, per query
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
@@ -212,8 +220,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       s[kb] = floatx16{};
       const uint32_t row = kb * 32 + c;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + k_swz(row, 2 * t + h)));
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DIM>(row, 2 * t + h)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[t], s[kb], 0, 0, 0);
       }
     }
@@ -229,14 +237,23 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                      auto mask_tag, bool& rescale) FA_INLINE -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;  // a row may see no key (yet)
+    // LOGIT: the tile's scores are first turned into log2-domain logits t
+    // (bias added, hidden keys set to -inf), so the max and the exponent use
+    // t directly and a hidden key gives exp2(-inf) = 0 whatever the scale
+    // (-inf * scale would be NaN for a zero scale).  Unmasked tiles without
+    // a bias keep the raw scores and fold the scale into one fma.
+    constexpr bool LOGIT = BIAS || MASK;
     float m_tile;
-    if constexpr (BIAS) {
-      // logits in log2 units: scale*log2(e)*s + log2(e)*bias
+    if constexpr (LOGIT) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
+          float t;
+          if constexpr (BIAS)
+            t = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
+          else
+            t = s[kb][r] * c_log2;
           if constexpr (MASK) {
             const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
             if (key > lim) t = -__builtin_inff();
@@ -250,15 +267,6 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[kb][r]);
       m_tile = wave_max_halves(ext);
     } else {
-      if constexpr (MASK) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > lim) s[kb][r] = NEG_SCALE ? __builtin_inff() : -__builtin_inff();
-          }
-      }
       float ext = s[0][0];
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -284,14 +292,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float x = BIAS ? s[kb][r] - m_use : __builtin_fmaf(s[kb][r], c_log2, -m_use);
-        float p = __builtin_amdgcn_exp2f(x);
-        if constexpr (MASK && !BIAS) {
-          // a hidden key's score is +-inf, and inf * scale is NaN when the
-          // scale is 0: zero it explicitly
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > lim) p = 0.0f;
-        }
+        const float x = LOGIT ? s[kb][r] - m_use : __builtin_fmaf(s[kb][r], c_log2, -m_use);
+        const float p = __builtin_amdgcn_exp2f(x);
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
@@ -307,7 +309,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int q4 = i16 & 3;           // which 4-column piece of the 16 columns
     const int hh = g >> 1;
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int d0 = cb * 32 + (g & 1) * 16 + q4 * 4;  // first of 4 d columns
       const uint32_t ch = (uint32_t)d0 >> 3;
       const uint32_t within = ((uint32_t)d0 & 7u) * 2u;
@@ -316,9 +318,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
         const uint32_t r1 = r0 + 8;
         const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r0, ch) + within));
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DIM>(r0, ch) + within));
         const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + v_swz(r1, ch) + within));
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DIM>(r1, ch) + within));
         // move the two 4-element results as whole dwords (no per-element
         // extraction): a = {lo[0..3], hi[0..3]}
         const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
@@ -331,7 +333,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   auto rescale_o = [&](float alpha) FA_INLINE {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NCB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
   };
@@ -351,7 +353,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles > 1) scores(kbuf(1), s1);
   }
   __syncthreads();  // K(0) consumed: K(2) goes into its buffer
-  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW>(rk, 2 * BC, kbuf(0), wave_u, lane);
+  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DIM>(rk, 2 * BC, kbuf(0), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
@@ -369,8 +371,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
     constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
-    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DIM>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DIM>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
     if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
     floatx16 s2[KB];
     if constexpr (HAS_S2) scores(kbuf(P), s2);
@@ -448,7 +450,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
   const int q = q0 + wave * 32 + c;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = cb * 32 + g4 * 8 + 4 * h;
@@ -461,7 +463,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         w0 = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
         w1 = (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16);
       }
-      __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, ro, (uint32_t)q * ROW_BYTES + d * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, ro, (uint32_t)q * RB + d * 2, 0, 0);
     }
   if (h == 0 && q < Nq) {
     const float ln2 = 0.69314718055994530942f;
@@ -469,9 +471,21 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-template <int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+template <int DIM, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
 const void* kernel_ptr() {
-  return (const void*)&fa_fwd_kernel<BC, NEG_SCALE, CAUSAL, BIAS>;
+  return (const void*)&fa_fwd_kernel<DIM, BC, NEG_SCALE, CAUSAL, BIAS>;
+}
+
+// Kernel for one head size: BC = 64 keys per tile (32 at head size 256, and
+// with a bias, whose tiles live in registers).
+template <int DIM>
+const void* select_kernel(bool neg, bool causal, bool bias) {
+  constexpr int BCP = DIM == 256 ? 32 : 64;
+  // the sign of the scale needs no variant with a bias: the max is taken
+  // over the biased logits themselves
+  if (bias) return causal ? kernel_ptr<DIM, 32, false, true, true>() : kernel_ptr<DIM, 32, false, false, true>();
+  if (causal) return neg ? kernel_ptr<DIM, BCP, true, true, false>() : kernel_ptr<DIM, BCP, false, true, false>();
+  return neg ? kernel_ptr<DIM, BCP, true, false, false>() : kernel_ptr<DIM, BCP, false, false, false>();
 }
 
 }  // namespace
@@ -493,16 +507,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
   float cl = c_log2;
   void* args[] = {&q, &k, &v, &o, &lse, &bias, &sb, &sh, &sq, &heads, &nq, &nk, &nqt, &cl};
   const bool neg = a.scale < 0.0f;
-  const void* fn;
-  if (bias) {
-    // the sign of the scale needs no variant here: the max is taken over the
-    // biased logits themselves
-    fn = a.causal ? kernel_ptr<32, false, true, true>() : kernel_ptr<32, false, false, true>();
-  } else if (a.causal) {
-    fn = neg ? kernel_ptr<64, true, true, false>() : kernel_ptr<64, false, true, false>();
-  } else {
-    fn = neg ? kernel_ptr<64, true, false, false>() : kernel_ptr<64, false, false, false>();
-  }
+  const void* fn = a.d == 64    ? select_kernel<64>(neg, a.causal, bias != nullptr)
+                   : a.d == 256 ? select_kernel<256>(neg, a.causal, bias != nullptr)
+                                : select_kernel<128>(neg, a.causal, bias != nullptr);
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }

@@ -13,6 +13,7 @@ struct LaunchArgs {
   void* O;
   float* LSE;
   int64_t BH, H, Nq, Nk;
+  int64_t d;            // head size: 64, 128 or 256
   float scale;
   bool causal;          // key j hidden from query i when j > i + Nk - Nq
   const float* bias;    // NULL, or fp32 bias[b*bias_sb + h*bias_sh + i*bias_sq + j]

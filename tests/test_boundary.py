@@ -49,7 +49,8 @@ def call(q=Qp, k=Kp, v=Vp, o=Op, lse=Lp, **kw):
     (dict(q=0), 1), (dict(k=0), 1), (dict(v=0), 1), (dict(o=0), 1), (dict(lse=0), 1),
     (dict(B=-1), 2), (dict(H=-1), 2), (dict(Nq=-1), 2), (dict(Nk=0), 2), (dict(Nk=-5), 2),
     (dict(B=1 << 40, H=1 << 40), 2),
-    (dict(d=64), 3), (dict(d=256), 3), (dict(Nq=(1 << 23) + 1), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(d=32), 3), (dict(d=96), 3), (dict(d=512), 3), (dict(Nq=(1 << 23) + 1), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(d=256, Nk=(1 << 22) + 1), 3), (dict(d=256, Nq=(1 << 22) + 1), 3),   # 2^31-byte head slices
     (dict(q=Qp + 8), 3), (dict(k=Kp + 2), 3), (dict(v=Vp + 4), 3), (dict(o=Op + 8), 3), (dict(lse=Lp + 2), 3),
     (dict(o=Qp), 4), (dict(o=Kp + 256), 4), (dict(lse=Vp + 1024), 4), (dict(lse=Op + 4096), 4),
     (dict(scale=float("nan")), 5), (dict(scale=float("inf")), 5), (dict(scale=float("-inf")), 5),
@@ -71,7 +72,7 @@ def test_masked_entry_validation():
     assert call_masked(causal=2) == 3
     assert call_masked(causal=-1) == 3
     assert call_masked(Nk=0) == 2
-    assert call_masked(d=64) == 3
+    assert call_masked(d=96) == 3
     assert call_masked(scale=float("nan")) == 5
     assert call_masked(Nq=0) == 0
     assert call_masked(Nq=0, bias=BIAS_P) == 0          # empty problem: no-op
@@ -155,7 +156,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dl=0), 1),
     (dict(B=-1), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2),
-    (dict(d=64), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(d=64), 3), (dict(d=256), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
     (dict(o=Op2 + 8), 3), (dict(dv=dVp + 4), 3), (dict(dl=Dp + 2), 3),
     (dict(dq=Qp), 4), (dict(dk=Kp + 256), 4), (dict(dv=dKp), 4), (dict(dl=Lp), 4), (dict(dq=dOp + 512), 4),
     (dict(scale=float("nan")), 5),
@@ -171,3 +172,11 @@ def test_bwd_accepted_arguments_reach_the_device_check():
         pytest.skip("would launch on fake pointers")
     assert call_bwd() == 6
     assert call_bwd(Nq=0) == 6     # dK and dV must still be zeroed on the device
+
+
+def test_other_head_sizes_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch on fake pointers")
+    for d in (64, 128, 256):
+        assert call(d=d) == 6

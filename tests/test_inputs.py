@@ -41,7 +41,8 @@ def test_workload_table():
     w = fi.WORKLOADS
     assert [(x.B, x.H, x.Nq, x.Nk, x.d) for x in w.values()] == [
         (1, 1, 256, 256, 128), (1, 8, 4096, 8192, 128), (4, 16, 4096, 4096, 128),
-        (2, 16, 8192, 8192, 128), (1, 16, 16384, 16384, 128)]
+        (2, 16, 8192, 8192, 128), (1, 16, 16384, 16384, 128), (2, 32, 8192, 8192, 64),
+        (2, 8, 8192, 8192, 256)]
     assert w["rtx5090_q4096_kv8192"].flops == 137438953472
     assert abs(w["tiny_256"].scale - 0.08838834764831845) < 1e-8
 
