@@ -12,7 +12,10 @@ additive bias and/or a causal mask), evaluated row by row in fp64 from the
 bf16 input bits.  Outputs: O in fp64 (never rounded to bf16) and the
 natural-log log-sum-exp of the scaled (and biased) logits per query row.
 The backward pass (dQ, dK, dV of a loss through O, given dO) is the chain
-rule of the same equations, also in fp64 (``attention_bwd*``).
+rule of the same equations, also in fp64 (``attention_bwd*``).  ``mx``
+holds the MXFP8 (OCP microscaling, E4M3 elements, E8M0 block scales)
+encoding used to prepare inputs of the MXFP8 path; attention on MXFP8 data
+is this same oracle applied to the exactly dequantized values.
 """
 from __future__ import annotations
 
