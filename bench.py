@@ -16,6 +16,7 @@ this host's cores).
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -31,6 +32,7 @@ if ROOT not in sys.path:
 import fa06_inputs as fi  # noqa: E402
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X published dense BF16 matrix peak
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X published dense FP8 matrix peak
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "b2_h16_n8192"
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
@@ -67,6 +69,9 @@ def parse():
                    help="time the backward pass (fa_bwd: dQ, dK, dV from dO, with O and LSE from one forward "
                         "call) instead of the forward; FLOP = 2.5x the forward's (five matrix products; the "
                         "kernels' recomputation of S and dP in the dQ pass is not counted)")
+    p.add_argument("--mxfp8", action="store_true",
+                   help="time the MXFP8 forward (fa_fwd_mxfp8) on the workload's Q, K, V quantized once by the "
+                        "library's GPU encoders (not timed); peak = dense FP8 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of attention, run a plain copy kernel (256 MiB read + 256 MiB "
@@ -204,6 +209,15 @@ def main():
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
     flop = 4 * w.B * w.H * w.d * visible_pairs(w.Nq, w.Nk, args.causal)
+    if args.mxfp8:
+        if bias is not None or args.bwd or w.d != 128:
+            raise SystemExit("--mxfp8 takes no bias, no --bwd and head size 128 only")
+        q8, qs, k8, ks, vt8, vs, _ = fa.mxfp8_inputs(q, k, v)
+        torch.cuda.synchronize()
+        call = lambda *a: fa.load_library().fa_fwd_mxfp8(*a)
+        call_args = (q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(), vt8.data_ptr(), vs.data_ptr(),
+                     o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, vt8.shape[3],
+                     ctypes.c_float(w.scale), int(args.causal), sptr)
     if args.bwd:
         if bias is not None:
             raise SystemExit("--bwd takes no bias")
@@ -246,15 +260,16 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (ev_ms * 1e-3) / 1e12
+    peak = MFMA_FP8_PEAK_TFLOPS if args.mxfp8 else MFMA_BF16_PEAK_TFLOPS
     roof = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
-        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "peak": peak,
         "unit": "TFLOP/s",
-        "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        "frac": round(achieved / peak, 4),
         "traffic": (MEASURED_TRAFFIC["bytes"]
                     if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
-                        and bias is None and w.name == MEASURED_TRAFFIC["workload"]) else None),
+                        and not args.mxfp8 and bias is None and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
     }
     out = {
@@ -268,14 +283,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "mxfp8 (e4m3 + e8m0)" if args.mxfp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name + ("+causal" if args.causal else "") +
-                   ("" if bias is None else f"+bias_{args.bias}") + ("+bwd" if args.bwd else ""), "B": w.B, "H": w.H,
+                   ("" if bias is None else f"+bias_{args.bias}") + ("+bwd" if args.bwd else "") +
+                   ("+mxfp8" if args.mxfp8 else ""), "B": w.B, "H": w.H,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": bool(args.causal), "bias": args.bias,
                    "flop_per_step": flop, "scale": w.scale, "seed": w.seed,
-                   "pct_of_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
-                   "kernel": fa.fa_bwd_build_info() if args.bwd else fa.fa_build_info()},
+                   "pct_of_peak": round(100 * value / (MFMA_FP8_PEAK_TFLOPS if args.mxfp8 else MFMA_BF16_PEAK_TFLOPS), 2),
+                   "kernel": (fa.fa_bwd_build_info() if args.bwd else
+                              fa.fa_mxfp8_build_info() if args.mxfp8 else fa.fa_build_info())},
         "roofline": roof,
         "cpu_baseline": None,
     }
@@ -283,7 +300,7 @@ def main():
         out["bias_bytes"] = bias.numel() * 4
     if args.bwd:
         out["roofline"]["note"] = "whole backward call (delta + dK/dV + dQ kernels); per-kernel split in profiles/"
-    if not args.no_cpu_baseline and bias is None and not args.bwd:
+    if not args.no_cpu_baseline and bias is None and not args.bwd and not args.mxfp8:
         cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse, causal=args.causal)
         out["cpu_baseline"] = cb
         out["parity_sampled"] = parity

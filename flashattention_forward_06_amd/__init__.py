@@ -71,6 +71,15 @@ def load_library(path: str | None = None):
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd_build_info.argtypes = []
     lib.fa_bwd_build_info.restype = ctypes.c_char_p
+    lib.fa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                 ctypes.c_int, vp]
+    lib.fa_fwd_mxfp8.restype = ctypes.c_int
+    lib.fa_mxfp8_quantize_rows.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.fa_mxfp8_quantize_rows.restype = ctypes.c_int
+    lib.fa_mxfp8_quantize_vt.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, vp]
+    lib.fa_mxfp8_quantize_vt.restype = ctypes.c_int
+    lib.fa_mxfp8_build_info.argtypes = []
+    lib.fa_mxfp8_build_info.restype = ctypes.c_char_p
     if path is None:
         _lib = lib
     return lib
@@ -253,5 +262,91 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
     return dq, dk, dv, delta
 
 
-__all__ = ["fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+def fa_mxfp8_build_info() -> str:
+    return load_library().fa_mxfp8_build_info().decode()
+
+
+def _check(rc):
+    if rc != 0:
+        raise FaError(rc, fa_status_string(rc))
+
+
+def _u8(name, t, shape, device):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.uint8 or tuple(t.shape) != tuple(shape) \
+            or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous uint8 tensor {tuple(shape)} on {device}")
+
+
+def mxfp8_quantize_rows(x, ld: int | None = None):
+    """bf16 [B, H, N, 128] -> (E4M3 [B, H, N, 128] uint8, E8M0 scales [B, H, ld, 4] uint8)."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.bfloat16 or x.dim() != 4 or not x.is_cuda \
+            or not x.is_contiguous():
+        raise ValueError("x must be a contiguous 4-D bfloat16 tensor on a HIP device")
+    B, H, N, d = x.shape
+    ld = N if ld is None else ld
+    e = torch.empty((B, H, N, d), dtype=torch.uint8, device=x.device)
+    sc = torch.zeros((B, H, ld, d // 32), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        _check(load_library().fa_mxfp8_quantize_rows(x.data_ptr(), e.data_ptr(), sc.data_ptr(), B, H, N, d, ld,
+                                                     torch.cuda.current_stream(x.device).cuda_stream))
+    return e, sc
+
+
+def mxfp8_quantize_vt(v, ldv: int | None = None):
+    """bf16 V [B, H, Nk, 128] -> (V^T E4M3 [B, H, 128, ldv], E8M0 [B, H, ldv/32, 128]); ldv defaults to
+    Nk rounded up to a multiple of 64."""
+    import torch
+    if not isinstance(v, torch.Tensor) or v.dtype != torch.bfloat16 or v.dim() != 4 or not v.is_cuda \
+            or not v.is_contiguous():
+        raise ValueError("v must be a contiguous 4-D bfloat16 tensor on a HIP device")
+    B, H, Nk, d = v.shape
+    ldv = (Nk + 63) // 64 * 64 if ldv is None else ldv
+    vt = torch.empty((B, H, d, ldv), dtype=torch.uint8, device=v.device)
+    vs = torch.empty((B, H, ldv // 32, d), dtype=torch.uint8, device=v.device)
+    with torch.cuda.device(v.device):
+        _check(load_library().fa_mxfp8_quantize_vt(v.data_ptr(), vt.data_ptr(), vs.data_ptr(), B, H, Nk, d, ldv,
+                                                   torch.cuda.current_stream(v.device).cuda_stream))
+    return vt, vs
+
+
+def mxfp8_inputs(q, k, v):
+    """Quantize bf16 q, k, v on the GPU into the arguments of fa_fwd_mxfp8:
+    (q8, qs, k8, ks, vt8, vs, Nk)."""
+    ldv = (k.shape[2] + 63) // 64 * 64
+    q8, qs = mxfp8_quantize_rows(q)
+    k8, ks = mxfp8_quantize_rows(k, ld=ldv)
+    vt8, vs = mxfp8_quantize_vt(v, ldv=ldv)
+    return q8, qs, k8, ks, vt8, vs, k.shape[2]
+
+
+def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, causal: bool = False,
+                 out=None, lse=None):
+    """Attention forward on MXFP8 inputs (layouts as returned by mxfp8_inputs).
+
+    Returns ``(o, lse)``: o [B, H, Nq, 128] bf16, lse [B, H, Nq] fp32."""
+    import torch
+    B, H, Nq, d = q8.shape
+    ldv = vt8.shape[3]
+    dev = q8.device
+    for name, t, shape in (("q8", q8, (B, H, Nq, d)), ("qs", qs, (B, H, Nq, d // 32)),
+                           ("k8", k8, (B, H, Nk, d)), ("ks", ks, (B, H, ldv, d // 32)),
+                           ("vt8", vt8, (B, H, d, ldv)), ("vs", vs, (B, H, ldv // 32, d))):
+        _u8(name, t, shape, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(load_library().fa_fwd_mxfp8(q8.data_ptr(), qs.data_ptr(), k8.data_ptr(), ks.data_ptr(),
+                                           vt8.data_ptr(), vs.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                           B, H, Nq, Nk, d, ldv, float(scale), int(bool(causal)),
+                                           torch.cuda.current_stream(dev).cuda_stream))
+    return out, lse
+
+
+__all__ = ["fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS"]

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa06.so")
-SOURCES = ["fa_api.cpp", "fa_fwd_kernel.hip", "fa_bwd_kernel.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd_kernel.hip", "fa_bwd_kernel.hip", "fa_fwd_mxfp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 instructions stay off: scalar float code only.

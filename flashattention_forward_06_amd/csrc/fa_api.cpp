@@ -189,6 +189,107 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   return FA_OK;
 }
 
+// ---------------------------------------------------------------- MXFP8
+namespace {
+constexpr int64_t kMaxLdv = int64_t(1) << 24;  // 128 rows of V^T stay within 2^31 bytes
+
+int check_mx_shapes(int64_t B, int64_t H, int64_t d) {
+  if (B < 0 || H < 0) return FA_ERR_INVALID_SHAPE;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
+  if (B * H > (INT64_MAX / 256) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
+  return FA_OK;
+}
+}  // namespace
+
+extern "C" int fa_fwd_mxfp8(const void* Q8, const void* Qs, const void* K8, const void* Ks, const void* Vt8,
+                            const void* Vs, void* O, float* LSE, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                            int64_t d, int64_t ldv, float scale, int causal, void* stream) {
+  int st = check_mx_shapes(B, H, d);
+  if (st != FA_OK) return st;
+  if (Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
+  if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  if (ldv < Nk || ldv % 64 != 0 || ldv > kMaxLdv) return FA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if ((BH * Nq > 0 && (!Q8 || !Qs || !O || !LSE)) || (BH > 0 && (!K8 || !Ks || !Vt8 || !Vs)))
+    return FA_ERR_NULL_POINTER;
+  if (BH * ((Nq + 127) / 128) > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_INVALID_SCALE;
+  if (!aligned(Q8, 16) || !aligned(K8, 16) || !aligned(Vt8, 16) || !aligned(Ks, 16) || !aligned(Vs, 16) ||
+      !aligned(Qs, 4) || !aligned(O, 16) || !aligned(LSE, 4))
+    return FA_ERR_UNSUPPORTED;
+  const int64_t o_bytes = BH * Nq * 256, l_bytes = BH * Nq * 4;
+  struct Buf {
+    const void* p;
+    int64_t n;
+  };
+  const Buf ins[] = {{Q8, BH * Nq * 128}, {Qs, BH * Nq * 4}, {K8, BH * Nk * 128}, {Ks, BH * ldv * 4},
+                     {Vt8, BH * 128 * ldv}, {Vs, BH * (ldv / 32) * 128}};
+  for (const Buf& i : ins)
+    if (overlaps(O, o_bytes, i.p, i.n) || overlaps(LSE, l_bytes, i.p, i.n)) return FA_ERR_ALIAS;
+  if (overlaps(O, o_bytes, LSE, l_bytes)) return FA_ERR_ALIAS;
+  if (BH * Nq == 0) return FA_OK;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  fa06::MxArgs a{};
+  a.Q8 = Q8;
+  a.Qs = Qs;
+  a.K8 = K8;
+  a.Ks = Ks;
+  a.Vt8 = Vt8;
+  a.Vs = Vs;
+  a.O = O;
+  a.LSE = LSE;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.ldv = ldv;
+  a.scale = scale;
+  a.causal = causal == 1;
+  if (fa06::launch_fa_fwd_mxfp8(a, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+extern "C" int fa_mxfp8_quantize_rows(const void* X, void* E, void* S, int64_t B, int64_t H, int64_t N, int64_t d,
+                                      int64_t ldS, void* stream) {
+  int st = check_mx_shapes(B, H, d);
+  if (st != FA_OK) return st;
+  if (N < 0 || ldS < N) return FA_ERR_INVALID_SHAPE;
+  if (N > FA_MAX_SEQ || ldS > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH * N > 0 && (!X || !E || !S)) return FA_ERR_NULL_POINTER;
+  if (!aligned(X, 16) || !aligned(E, 16)) return FA_ERR_UNSUPPORTED;
+  const int64_t x_bytes = BH * N * 256, e_bytes = BH * N * 128, s_bytes = BH * ldS * 4;
+  if (overlaps(E, e_bytes, X, x_bytes) || overlaps(S, s_bytes, X, x_bytes) || overlaps(S, s_bytes, E, e_bytes))
+    return FA_ERR_ALIAS;
+  if (BH * N == 0) return FA_OK;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  return fa06::launch_mx_quantize_rows(X, E, S, BH, N, ldS, static_cast<hipStream_t>(stream)) == 0 ? FA_OK
+                                                                                                 : FA_ERR_LAUNCH;
+}
+
+extern "C" int fa_mxfp8_quantize_vt(const void* V, void* Vt, void* Vs, int64_t B, int64_t H, int64_t Nk, int64_t d,
+                                    int64_t ldv, void* stream) {
+  int st = check_mx_shapes(B, H, d);
+  if (st != FA_OK) return st;
+  if (Nk < 1) return FA_ERR_INVALID_SHAPE;
+  if (Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (ldv < Nk || ldv % 64 != 0 || ldv > kMaxLdv) return FA_ERR_UNSUPPORTED;
+  const int64_t BH = B * H;
+  if (BH > 0 && (!V || !Vt || !Vs)) return FA_ERR_NULL_POINTER;
+  if (!aligned(V, 2) || !aligned(Vt, 16)) return FA_ERR_UNSUPPORTED;
+  const int64_t v_bytes = BH * Nk * 256, t_bytes = BH * 128 * ldv, s_bytes = BH * (ldv / 32) * 128;
+  if (overlaps(Vt, t_bytes, V, v_bytes) || overlaps(Vs, s_bytes, V, v_bytes) || overlaps(Vs, s_bytes, Vt, t_bytes))
+    return FA_ERR_ALIAS;
+  if (BH == 0) return FA_OK;
+  const int dev = check_device();
+  if (dev != FA_OK) return dev;
+  return fa06::launch_mx_quantize_vt(V, Vt, Vs, BH, Nk, ldv, static_cast<hipStream_t>(stream)) == 0 ? FA_OK
+                                                                                                  : FA_ERR_LAUNCH;
+}
+
 extern "C" const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -208,3 +309,5 @@ extern "C" const char* fa_status_string(int status) {
 extern "C" const char* fa_build_info(void) { return fa06::kernel_config_string(); }
 
 extern "C" const char* fa_bwd_build_info(void) { return fa06::bwd_config_string(); }
+
+extern "C" const char* fa_mxfp8_build_info(void) { return fa06::mxfp8_config_string(); }

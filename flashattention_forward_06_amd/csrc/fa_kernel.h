@@ -45,4 +45,23 @@ struct BwdArgs {
 int launch_fa_bwd(const BwdArgs& args, hipStream_t stream);
 const char* bwd_config_string();
 
+// One MXFP8 forward call (head size 128), already validated.
+struct MxArgs {
+  const void* Q8;   // [BH, Nq, 128] E4M3
+  const void* Qs;   // [BH, Nq, 4] E8M0
+  const void* K8;   // [BH, Nk, 128] E4M3
+  const void* Ks;   // [BH, ldv, 4] E8M0 (rows >= Nk unused)
+  const void* Vt8;  // [BH, 128, ldv] E4M3, keys >= Nk zero
+  const void* Vs;   // [BH, ldv/32, 128] E8M0
+  void* O;          // [BH, Nq, 128] bf16
+  float* LSE;       // [BH, Nq]
+  int64_t BH, Nq, Nk, ldv;
+  float scale;
+  bool causal;
+};
+int launch_fa_fwd_mxfp8(const MxArgs& args, hipStream_t stream);
+int launch_mx_quantize_rows(const void* X, void* E, void* S, int64_t BH, int64_t N, int64_t ldS, hipStream_t stream);
+int launch_mx_quantize_vt(const void* V, void* Vt, void* Vs, int64_t BH, int64_t Nk, int64_t ldv, hipStream_t stream);
+const char* mxfp8_config_string();
+
 }  // namespace fa06

@@ -151,6 +151,52 @@ int fa_bwd(const void *Q, const void *K, const void *V, const void *O, const voi
            int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
            int causal, void *stream);
 
+/*
+ * MXFP8 attention.  The forward pass of fa_fwd_masked (no bias) on inputs in
+ * the OCP microscaling format MXFP8: E4M3 elements, and one E8M0 scale byte
+ * (value 2^(s-127); s = 255 is NaN) per block of 32 elements along the
+ * contraction axis of each product -- along the head dimension for Q and K,
+ * along the keys for V, which is therefore passed transposed.  The pages
+ * name MXFP8 attention as the aim of their kernel work ("Flash Attention на
+ * 5090 в CUDA C++": motivation, "Что дальше") without defining it; the
+ * format is the OCP one.  Head size 128 only.
+ *
+ * fa_fwd_mxfp8 -- device buffers, u8 unless stated:
+ *   Q8 [B,H,Nq,128] E4M3 and Qs [B,H,Nq,4] E8M0 (Qs 4-byte aligned);
+ *   K8 [B,H,Nk,128] E4M3 and Ks [B,H,ldv,4] E8M0 (rows >= Nk unused);
+ *   Vt8 [B,H,128,ldv] E4M3, V transposed, keys >= Nk holding finite values
+ *     (zeros); Vs [B,H,ldv/32,128] E8M0, Vs[b,h,j,c] scaling keys
+ *     32j..32j+31 of column c;
+ *   O [B,H,Nq,128] bf16 and LSE [B,H,Nq] fp32 as for fa_fwd;
+ *   ldv: multiple of 64, Nk <= ldv <= 2^24.
+ * The kernel computes S on the block-scaled MFMA, P in fp32, rounds P to
+ * E4M3 (scale 1) for the P V product and normalises by the fp32 row sum.
+ * Every pointer 16-byte aligned except Qs and LSE (4); errors and execution
+ * as for fa_fwd_masked.
+ */
+int fa_fwd_mxfp8(const void *Q8, const void *Qs, const void *K8, const void *Ks, const void *Vt8,
+                 const void *Vs, void *O, float *LSE, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                 int64_t d, int64_t ldv, float scale, int causal, void *stream);
+
+/*
+ * fa_mxfp8_quantize_rows -- bf16 X [B,H,N,128] to MXFP8 along the last axis:
+ * E [B,H,N,128] E4M3 and S [B,H,ldS,4] E8M0 (ldS >= N; for K pass ldS = ldv).
+ * Each block of 32 gets the scale 2^(floor(log2 max|x|) - 8) (2^-127 for an
+ * all-zero block); elements are x / scale rounded to the nearest E4M3 value
+ * (ties to even), magnitudes above 448 saturating.  X and E 16-byte aligned.
+ *
+ * fa_mxfp8_quantize_vt -- bf16 V [B,H,Nk,128] to the V^T layout of
+ * fa_fwd_mxfp8: Vt [B,H,128,ldv] (keys >= Nk written as zeros) and
+ * Vs [B,H,ldv/32,128], blocks of 32 keys per column, same rules.  ldv a
+ * multiple of 64, Nk <= ldv <= 2^24; Vt 16-byte aligned.
+ *
+ * Both enqueue one kernel on `stream`; errors as for fa_fwd.
+ */
+int fa_mxfp8_quantize_rows(const void *X, void *E, void *S, int64_t B, int64_t H, int64_t N, int64_t d,
+                           int64_t ldS, void *stream);
+int fa_mxfp8_quantize_vt(const void *V, void *Vt, void *Vs, int64_t B, int64_t H, int64_t Nk, int64_t d,
+                         int64_t ldv, void *stream);
+
 /* fa_status_string -- static, NUL-terminated description of a status code. */
 const char *fa_status_string(int status);
 
@@ -159,6 +205,9 @@ const char *fa_build_info(void);
 
 /* fa_bwd_build_info -- static string naming the backward kernels' configuration. */
 const char *fa_bwd_build_info(void);
+
+/* fa_mxfp8_build_info -- static string naming the MXFP8 kernel's configuration. */
+const char *fa_mxfp8_build_info(void);
 
 #ifdef __cplusplus
 }

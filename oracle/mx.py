@@ -84,8 +84,9 @@ def mx_quantize(x: np.ndarray):
         raise ValueError(f"last axis ({n}) must be a multiple of {BLOCK}")
     blocks = x.reshape(*x.shape[:-1], n // BLOCK, BLOCK)
     amax = np.abs(blocks).max(axis=-1)
-    with np.errstate(divide="ignore"):
-        shared = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - E4M3_EMAX, -127)
+    # floor(log2 amax) exactly: amax = m * 2^e with m in [0.5, 1)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    shared = np.where(amax > 0, e.astype(np.int64) - 1 - E4M3_EMAX, -127)
     shared = np.clip(shared, -127, 127).astype(np.int64)
     elems = e4m3_encode(blocks / np.ldexp(1.0, shared)[..., None])
     return elems.reshape(x.shape), (shared + 127).astype(np.uint8)

@@ -21,7 +21,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_masked", "fa_status_string"]
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_masked", "fa_fwd_mxfp8",
+                     "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
 
@@ -180,3 +181,41 @@ def test_other_head_sizes_reach_the_device_check():
         pytest.skip("would launch on fake pointers")
     for d in (64, 128, 256):
         assert call(d=d) == 6
+
+
+# MXFP8 entry: fake buffers
+Q8p, QSp, K8p, KSp, VTp, VSp = 0xD0000000, 0xD8000000, 0xE0000000, 0xE8000000, 0xF0000000, 0xF8000000
+GOOD_MX = dict(q8=Q8p, qs=QSp, k8=K8p, ks=KSp, vt=VTp, vs=VSp, o=Op, lse=Lp,
+               B=1, H=2, Nq=256, Nk=200, d=128, ldv=256, scale=0.088, causal=0)
+
+
+def call_mx(**kw):
+    a = {**GOOD_MX, **kw}
+    return fa.load_library().fa_fwd_mxfp8(a["q8"], a["qs"], a["k8"], a["ks"], a["vt"], a["vs"], a["o"], a["lse"],
+                                          a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["ldv"],
+                                          ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q8=0), 1), (dict(vs=0), 1), (dict(lse=0), 1),
+    (dict(Nk=0), 2), (dict(B=-1), 2),
+    (dict(d=64), 3), (dict(ldv=192), 3), (dict(ldv=100), 3), (dict(ldv=(1 << 24) + 64), 3), (dict(causal=3), 3),
+    (dict(qs=QSp + 2), 3), (dict(ks=KSp + 4), 3), (dict(vt=VTp + 8), 3),
+    (dict(o=Q8p), 4), (dict(lse=VSp), 4),
+    (dict(scale=float("inf")), 5),
+    (dict(Nq=0), 0),
+])
+def test_mxfp8_validation_codes(kw, code):
+    assert call_mx(**kw) == code
+
+
+def test_mxfp8_quantize_validation_codes():
+    lib = fa.load_library()
+    assert lib.fa_mxfp8_quantize_rows(Qp, Q8p, QSp, 1, 2, 256, 64, 256, None) == 3      # d must be 128
+    assert lib.fa_mxfp8_quantize_rows(Qp, Q8p, QSp, 1, 2, 256, 128, 100, None) == 2     # ldS < N
+    assert lib.fa_mxfp8_quantize_rows(Qp + 2, Q8p, QSp, 1, 2, 256, 128, 256, None) == 3
+    assert lib.fa_mxfp8_quantize_rows(Qp, Qp, QSp, 1, 2, 256, 128, 256, None) == 4      # E overlaps X
+    assert lib.fa_mxfp8_quantize_rows(Qp, Q8p, QSp, 1, 2, 0, 128, 0, None) == 0         # empty
+    assert lib.fa_mxfp8_quantize_vt(Vp, VTp, VSp, 1, 2, 200, 128, 224, None) == 3       # ldv not a multiple of 64
+    assert lib.fa_mxfp8_quantize_vt(Vp, VTp, VSp, 1, 2, 300, 128, 256, None) == 3       # ldv < Nk
+    assert lib.fa_mxfp8_quantize_vt(Vp, Vp, VSp, 1, 2, 200, 128, 256, None) == 4
