@@ -28,6 +28,13 @@
 // S and dP are computed in both the dK/dV and the dQ kernel (seven matrix
 // products instead of five) in exchange for no atomic accumulation of dQ.
 // Tiles read both row-wise and transposed use the SWZ_BOTH swizzle.
+// Both matrix kernels run one wave per SIMD (their accumulators and
+// register-resident operands need ~350 registers), so all overlap of VALU
+// and MFMA work is inside the wave: each step computes two 32-row (or
+// 32-key) sub-blocks, issues the products of the second before the
+// softmax-gradient arithmetic of the first, and sched_group_barrier pins an
+// interleave of one MFMA to a few VALU instructions (6 in dK/dV; 5 and 12
+// in dQ, chosen by timing).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -156,8 +163,10 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     dkacc[i] = floatx16{};
   }
 
-  // One block of 64 query rows, as two sub-blocks of 32.
-  auto step = [&](int qb, int st, auto mask_tag) FA_INLINE {
+  // Causal kernel: one block of 64 query rows as two sub-blocks of 32, in
+  // order (the pipelined form needs more registers than a wave has once
+  // the masked steps are in the same kernel).
+  auto step_seq = [&](int qb, int st, auto mask_tag) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* qs = qbuf0 + st * KV_TILE;
     const char* ds = dobuf0 + st * KV_TILE;
@@ -203,16 +212,92 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   };
 
+  // One block of 64 query rows as two sub-blocks of 32, software pipelined
+  // inside the wave: S/dP of sub-block 1 are issued before the P/dS of
+  // sub-block 0, and dV/dK of sub-block 0 before the P/dS of sub-block 1.
+  auto sdp = [&](const char* qs, const char* ds, int ib, floatx16& s, floatx16& dp) FA_INLINE {
+    s = floatx16{};
+    dp = floatx16{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0, 0);
+  };
+  auto pds = [&](const char* ls, const char* dls, int qb, int ib, const floatx16& s, const floatx16& dp,
+                 auto mask_tag, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) FA_INLINE {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // accumulator register r holds row ib*32 + 8(r/4) + 4h + r%4 of the
+    // block; the key is hidden from that row when 8(r/4) + r%4 < kd
+    const int kd = key - off - qb * KV_QB - ib * 32 - 4 * h;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 l4 = *reinterpret_cast<const floatx4*>(ls + (ib * 32 + 8 * g + 4 * h) * 4);
+      const floatx4 d4 = *reinterpret_cast<const floatx4*>(dls + (ib * 32 + 8 * g + 4 * h) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * LOG2E));
+        if constexpr (MASK) {
+          if (8 * g + e < kd) p = 0.0f;
+        }
+        const float dsv = p * (dp[r] - d4[e]);
+        pb[r >> 3][r & 7] = (__bf16)p;
+        dsb[r >> 3][r & 7] = (__bf16)dsv;
+      }
+    }
+  };
+  auto dvdk = [&](const char* qs, const char* ds, int ib, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) FA_INLINE {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ds, ib * 32 + ks * 16, cb, lane),
+                                                            pb[ks], dvacc[cb], 0, 0, 0);
+        dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(qs, ib * 32 + ks * 16, cb, lane),
+                                                            dsb[ks], dkacc[cb], 0, 0, 0);
+      }
+  };
+  auto step = [&](int qb, int st, auto mask_tag) FA_INLINE {
+    const char* qs = qbuf0 + st * KV_TILE;
+    const char* ds = dobuf0 + st * KV_TILE;
+    const char* ls = lbuf0 + st * KV_QB * 4;
+    const char* dls = dbuf0 + st * KV_QB * 4;
+    floatx16 s0, dp0, s1, dp1;
+    bf16x8 p0[2], g0[2], p1[2], g1[2];
+    sdp(qs, ds, 0, s0, dp0);
+    sdp(qs, ds, 1, s1, dp1);
+    pds(ls, dls, qb, 0, s0, dp0, mask_tag, p0, g0);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    dvdk(qs, ds, 0, p0, g0);
+    pds(ls, dls, qb, 1, s1, dp1, mask_tag, p1, g1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+    dvdk(qs, ds, 1, p1, g1);
+  };
+
   if (qb_first < n_qb) stage_in(qb_first, 0);
   for (int qb = qb_first; qb < n_qb; ++qb) {
     const int st = (qb - qb_first) & 1;
     wait_vmem();
     __syncthreads();  // stage st landed for every wave; stage st^1 is free
     if (qb + 1 < n_qb) stage_in(qb + 1, st ^ 1);
-    if (CAUSAL && qb < qb_unmasked)
-      step(qb, st, std::true_type{});
-    else
+    if constexpr (CAUSAL) {
+      if (qb < qb_unmasked)
+        step_seq(qb, st, std::true_type{});
+      else
+        step_seq(qb, st, std::false_type{});
+    } else {
       step(qb, st, std::false_type{});
+    }
   }
 
 #pragma unroll
@@ -300,40 +385,62 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     tile_to_lds<DQ_BC, SWZ_ROW>(rv, (uint32_t)(j * DQ_BC), vbuf0 + st * DQ_TILE, wave_u, lane);
   };
 
-  // One K/V tile, as two 32-key blocks (short live ranges: S, dP and dS of
-  // one block at a time).
-  auto step = [&](int j, int st, auto mask_tag) FA_INLINE {
+  // One K/V tile as two 32-key blocks, software pipelined inside the wave:
+  // S/dP of block 1 are issued before the softmax of block 0, and dQ of
+  // block 0 before the softmax of block 1, so the VALU work overlaps MFMAs.
+  auto sdp = [&](const char* ks, const char* vs, int kb, floatx16& s, floatx16& dp) FA_INLINE {
+    s = floatx16{};
+    dp = floatx16{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
+  };
+  auto dsoft = [&](const floatx16& s, const floatx16& dp, int kb, int lim, auto mask_tag, bf16x8 (&dsb)[2]) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, nl2));
+      if constexpr (MASK) {
+        const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (kk > lim) p = 0.0f;
+      }
+      dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
+    }
+  };
+  auto dq_acc = [&](const char* ks, int kb, const bf16x8 (&dsb)[2]) FA_INLINE {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2)
+        dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ks, kb * 32 + k2 * 16, cb, lane),
+                                                            dsb[k2], dqacc[cb], 0, 0, 0);
+  };
+  auto step = [&](int j, int st, auto mask_tag) FA_INLINE {
     const char* ks = kbuf0 + st * DQ_TILE;
     const char* vs = vbuf0 + st * DQ_TILE;
     const int lim = key_lim - j * DQ_BC;
+    floatx16 s0, dp0, s1, dp1;
+    bf16x8 ds0[2], ds1[2];
+    sdp(ks, vs, 0, s0, dp0);
+    sdp(ks, vs, 1, s1, dp1);
+    dsoft(s0, dp0, 0, lim, mask_tag, ds0);
+    // 16 MFMAs of S/dP(1), each followed by 6 VALU of the softmax of block 0
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      floatx16 s = floatx16{}, dp = floatx16{};
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
-      // register r holds key kb*32 + 8(r/4) + 4h + r%4 of the tile
-      bf16x8 dsb[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, nl2));
-        if constexpr (MASK) {
-          const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (kk > lim) p = 0.0f;
-        }
-        dsb[r >> 3][r & 7] = (__bf16)(p * (dp[r] - dq_d));
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2)
-          dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              tr_read_a<SWZ_BOTH>(ks, kb * 32 + k2 * 16, cb, lane), dsb[k2], dqacc[cb], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
+    dq_acc(ks, 0, ds0);
+    dsoft(s1, dp1, 1, lim, mask_tag, ds1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    }
+    dq_acc(ks, 1, ds1);
   };
 
   if (n_tiles > 0) stage_in(0, 0);
@@ -395,8 +502,8 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 }
 
 const char* bwd_config_string() {
-  return "gfx950 fa_bwd v1: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
-         "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); no atomics";
+  return "gfx950 fa_bwd v2: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
+         "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave; no atomics";
 }
 
 }  // namespace fa06
