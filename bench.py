@@ -113,7 +113,7 @@ def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
 def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
     import oracle
     import torch
-    per_row_flop = 4 * w.Nk * w.d
+    per_row_flop = 2 * w.Nk * (w.d + w.d_v)
     total_rows = w.B * w.H * w.Nq
     rng = np.random.default_rng(w.seed + 17)
     # calibrate on a small sample, then size the timed sample to ~target_s
@@ -129,7 +129,7 @@ def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
         if not causal:
             return len(rows) * per_row_flop
         i = rows % w.Nq
-        return int(np.clip(i + (w.Nk - w.Nq) + 1, 0, w.Nk).sum()) * 4 * w.d
+        return int(np.clip(i + (w.Nk - w.Nq) + 1, 0, w.Nk).sum()) * 2 * (w.d + w.d_v)
 
     t0 = time.perf_counter()
     run(rows0)
@@ -150,7 +150,7 @@ def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
     parity = None
     if o_gpu is not None:
         idx = torch.from_numpy(rows).to(o_gpu.device)
-        og = o_gpu.view(-1, w.d)[idx].float().cpu().numpy().astype(np.float64)
+        og = o_gpu.view(-1, w.d_v)[idx].float().cpu().numpy().astype(np.float64)
         lg = lse_gpu.view(-1)[idx].cpu().numpy().astype(np.float64)
         dO = np.abs(og - Oo)
         parity = {"rows": n, "max_abs_dO": float(dO.max()), "mean_abs_dO": float(dO.mean()),
@@ -180,7 +180,7 @@ def main():
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = up(Q), up(K), up(V)
-    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((w.B, w.H, w.Nq, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
@@ -198,7 +198,13 @@ def main():
         sb, sh, sq = w.H * w.Nk, w.Nk, 0
     if bias is not None and (w.Nk % 4 or bias.data_ptr() % 16):
         raise SystemExit("bias rows must be 16-byte aligned (Nk a multiple of 4)")
-    if args.causal or bias is not None:
+    if w.d_v != w.d:
+        call = fa.fa_fwd_dv_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.d_v, w.scale, int(args.causal),
+                     None if bias is None else bias.data_ptr(), *((sb, sh, sq) if bias is not None else (0, 0, 0)),
+                     sptr)
+    elif args.causal or bias is not None:
         call = fa.fa_fwd_masked_raw
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal),
@@ -208,9 +214,9 @@ def main():
         call = fa.fa_fwd_raw
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.Nq, w.Nk, w.d, w.scale, sptr)
-    flop = 4 * w.B * w.H * w.d * visible_pairs(w.Nq, w.Nk, args.causal)
+    flop = 2 * w.B * w.H * (w.d + w.d_v) * visible_pairs(w.Nq, w.Nk, args.causal)
     if args.mxfp8:
-        if bias is not None or args.bwd or w.d != 128:
+        if bias is not None or args.bwd or w.d != 128 or w.d_v != 128:
             raise SystemExit("--mxfp8 takes no bias, no --bwd and head size 128 only")
         q8, qs, k8, ks, vt8, vs, _ = fa.mxfp8_inputs(q, k, v)
         torch.cuda.synchronize()
@@ -219,8 +225,8 @@ def main():
                      o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, vt8.shape[3],
                      ctypes.c_float(w.scale), int(args.causal), sptr)
     if args.bwd:
-        if bias is not None:
-            raise SystemExit("--bwd takes no bias")
+        if bias is not None or w.d != 128 or w.d_v != 128:
+            raise SystemExit("--bwd takes no bias and head size 128 only")
         dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d, seed=w.seed + 5000)[0]
         g = up(dO)
         rc = call(*call_args)  # forward once: O and LSE
@@ -288,7 +294,7 @@ def main():
         "config": {"workload": w.name + ("+causal" if args.causal else "") +
                    ("" if bias is None else f"+bias_{args.bias}") + ("+bwd" if args.bwd else "") +
                    ("+mxfp8" if args.mxfp8 else ""), "B": w.B, "H": w.H,
-                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": bool(args.causal), "bias": args.bias,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "d_v": w.d_v, "causal": bool(args.causal), "bias": args.bias,
                    "flop_per_step": flop, "scale": w.scale, "seed": w.seed,
                    "pct_of_peak": round(100 * value / (MFMA_FP8_PEAK_TFLOPS if args.mxfp8 else MFMA_BF16_PEAK_TFLOPS), 2),
                    "kernel": (fa.fa_bwd_build_info() if args.bwd else

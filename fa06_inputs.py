@@ -59,6 +59,11 @@ class Workload:
     k_scale: float = 1.0
     offset_frac: float = 0.0
     offset: float = 0.0
+    dv: int | None = None   # value head size; None: equal to d
+
+    @property
+    def d_v(self) -> int:
+        return self.d if self.dv is None else self.dv
 
     @property
     def scale(self) -> float:
@@ -67,11 +72,13 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        """Two dense products per (query, key) pair: 4*B*H*Nq*Nk*d."""
-        return 4 * self.B * self.H * self.Nq * self.Nk * self.d
+        """Two dense products per (query, key) pair: 2*B*H*Nq*Nk*(d + d_v)
+        (4*B*H*Nq*Nk*d when d_v = d)."""
+        return 2 * self.B * self.H * self.Nq * self.Nk * (self.d + self.d_v)
 
     def describe(self) -> str:
-        s = f"B={self.B} H={self.H} Nq={self.Nq} Nk={self.Nk} d={self.d} seed={self.seed}"
+        dv = "" if self.dv is None else f" d_v={self.dv}"
+        s = f"B={self.B} H={self.H} Nq={self.Nq} Nk={self.Nk} d={self.d}{dv} seed={self.seed}"
         if self.k_scale != 1.0 or self.offset_frac:
             s += f" K*{self.k_scale:g} +{self.offset:g} on {self.offset_frac:.0%} of rows"
         return s
@@ -80,7 +87,8 @@ class Workload:
 # The workloads: a tiny case, the RTX 5090 benchmark shape (bs=1, heads=8,
 # q=4096, kv=8192), and 16K tokens at 4K/8K/16K sequence length with 16
 # heads of size 128 (the 16K one stresses large logits and running-max
-# jumps); then head sizes 64 and 256 at 8K.
+# jumps); then head sizes 64 and 256 at 8K, and query/key head size 192 with
+# value head size 128 (the split of multi-head latent attention's prefill).
 WORKLOADS = {
     "tiny_256": Workload("tiny_256", 1, 1, 256, 256, seed=1001),
     "rtx5090_q4096_kv8192": Workload("rtx5090_q4096_kv8192", 1, 8, 4096, 8192, seed=1002),
@@ -92,6 +100,7 @@ WORKLOADS = {
     # other head sizes at the same hidden size H*d = 2048 and 16K tokens
     "b2_h32_n8192_d64": Workload("b2_h32_n8192_d64", 2, 32, 8192, 8192, d=64, seed=1006),
     "b2_h8_n8192_d256": Workload("b2_h8_n8192_d256", 2, 8, 8192, 8192, d=256, seed=1007),
+    "b2_h16_n8192_d192_dv128": Workload("b2_h16_n8192_d192_dv128", 2, 16, 8192, 8192, d=192, seed=1008, dv=128),
 }
 WORKLOAD_ORDER = list(WORKLOADS)
 
@@ -121,7 +130,7 @@ def make_qkv(B: int, H: int, Nq: int, Nk: int, d: int = HEAD_DIM, seed: int = 0,
 
 
 def make_workload(w: Workload):
-    return make_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.seed, w.k_scale, w.offset_frac, w.offset)
+    return make_qkv(w.B, w.H, w.Nq, w.Nk, w.d, w.seed, w.k_scale, w.offset_frac, w.offset, dv=w.dv)
 
 
 def sample_rows(B: int, H: int, Nq: int, n: int, seed: int) -> np.ndarray:

@@ -62,6 +62,9 @@ def load_library(path: str | None = None):
     lib.fa_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                   ctypes.c_int, vp, i64, i64, i64, vp]
     lib.fa_fwd_masked.restype = ctypes.c_int
+    lib.fa_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                              ctypes.c_int, vp, i64, i64, i64, vp]
+    lib.fa_fwd_dv.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_build_info.argtypes = []
@@ -120,6 +123,14 @@ def fa_fwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: i
                                         ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq, stream)
 
 
+def fa_fwd_dv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                  B: int, H: int, Nq: int, Nk: int, d: int, dv: int, scale: float, causal: int,
+                  bias_ptr: int | None, sb: int, sh: int, sq: int, stream: int) -> int:
+    """Direct call of the C ``fa_fwd_dv``; returns the status."""
+    return load_library().fa_fwd_dv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
+                                    ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq, stream)
+
+
 def _bias_arg(bias, B: int, H: int, Nq: int, Nk: int, device):
     """Bias tensor -> (tensor kept alive, element strides) in the layout the
     library reads: unit key stride and row/head/batch strides that are
@@ -155,13 +166,14 @@ def _bias_arg(bias, B: int, H: int, Nq: int, Nk: int, device):
 def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False, bias=None):
     """Fused attention forward on torch tensors.
 
-    q: [B, H, Nq, 128] bf16, k and v: [B, H, Nk, 128] bf16, all contiguous on
-    the same HIP device.  ``scale`` defaults to 1/sqrt(128).  With
+    q: [B, H, Nq, d] bf16, k: [B, H, Nk, d], v: [B, H, Nk, dv] bf16, all
+    contiguous on the same HIP device; (d, dv) is (64, 64), (128, 128),
+    (256, 256) or (192, 128).  ``scale`` defaults to 1/sqrt(d).  With
     ``causal``, key j is hidden from query i when j > i + (Nk - Nq).
     ``bias`` (optional) is an fp32 tensor broadcastable to [B, H, Nq, Nk],
     added to the scaled scores.  Rows that see no key (causal with Nq > Nk,
     or a bias of -inf on every key) give O = 0, LSE = -inf.  Returns
-    ``(o, lse)``: o [B, H, Nq, 128] bf16 and lse [B, H, Nq] fp32.  Optional
+    ``(o, lse)``: o [B, H, Nq, dv] bf16 and lse [B, H, Nq] fp32.  Optional
     ``out`` / ``lse`` tensors of those shapes receive the results.  The call is
     enqueued on the current stream of q's device.
     """
@@ -181,16 +193,17 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k and v must be on the same device")
     B, H, Nq, d = q.shape
-    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or tuple(v.shape) != tuple(k.shape):
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or tuple(v.shape[:3]) != tuple(k.shape[:3]):
         raise ValueError(f"shape mismatch: q{tuple(q.shape)} k{tuple(k.shape)} v{tuple(v.shape)}")
     Nk = k.shape[2]
+    dv = v.shape[3]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.bfloat16, device=q.device)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, Nq, d) or not out.is_contiguous() \
+        out = torch.empty((B, H, Nq, dv), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, Nq, dv) or not out.is_contiguous() \
             or out.device != q.device:
-        raise ValueError("out must be a contiguous bf16 tensor [B, H, Nq, d] on q's device")
+        raise ValueError("out must be a contiguous bf16 tensor [B, H, Nq, dv] on q's device")
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     elif lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous() \
@@ -201,7 +214,11 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
         bias_t, sb, sh, sq = _bias_arg(bias, B, H, Nq, Nk, q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
-        if causal or bias_t is not None:
+        if dv != d:
+            rc = fa_fwd_dv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, H, Nq, Nk, d, dv, float(scale), int(bool(causal)),
+                               None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, stream)
+        elif causal or bias_t is not None:
             rc = fa_fwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                    B, H, Nq, Nk, d, float(scale), int(bool(causal)),
                                    None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, stream)

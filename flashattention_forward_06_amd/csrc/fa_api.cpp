@@ -52,18 +52,24 @@ constexpr int64_t kBiasWaveSpan = int64_t(1) << 29;
 // Largest bias extent over all (b, h, i, j), in elements.
 constexpr int64_t kBiasMaxExtent = int64_t(1) << 60;
 
+// (d, dv) pairs with a kernel: equal head sizes 64, 128, 256, and the split
+// 192 / 128 of multi-head latent attention's prefill.
+bool head_sizes_supported(int64_t d, int64_t dv) {
+  return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
+}
+
 int validate_and_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
-                        int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
-                        int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
+                        int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal,
+                        const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
-  if (Nq > max_seq(d) || Nk > max_seq(d)) return FA_ERR_UNSUPPORTED;
+  if (!head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
+  const int64_t dmax = d > dv ? d : dv;
+  if (Nq > max_seq(dmax) || Nk > max_seq(dmax)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   // sizes: B*H*N*d*2 bytes must fit in int64 (N*d*2 <= 2^31)
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
-  const int64_t row_bytes = d * 2;
-  if (BH > (INT64_MAX / row_bytes) / max_seq(d)) return FA_ERR_INVALID_SHAPE;
+  if (BH > (INT64_MAX / (dmax * 2)) / max_seq(dmax)) return FA_ERR_INVALID_SHAPE;
   // bias: non-negative element strides; the extent must be addressable
   int64_t bias_elems = 0;
   if (bias != nullptr) {
@@ -86,12 +92,13 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
   // the bias is read 16 bytes (4 keys) at a time: rows start 16-byte aligned
   if (bias != nullptr && (!aligned(bias, 16) || bias_sb % 4 != 0 || bias_sh % 4 != 0 || bias_sq % 4 != 0))
     return FA_ERR_UNSUPPORTED;
-  const int64_t q_bytes = BH * Nq * row_bytes, kv_bytes = BH * Nk * row_bytes, l_bytes = BH * Nq * 4;
+  const int64_t q_bytes = BH * Nq * d * 2, k_bytes = BH * Nk * d * 2, v_bytes = BH * Nk * dv * 2;
+  const int64_t o_bytes = BH * Nq * dv * 2, l_bytes = BH * Nq * 4;
   const int64_t b_bytes = bias_elems * 4;
-  if (overlaps(O, q_bytes, Q, q_bytes) || overlaps(O, q_bytes, K, kv_bytes) || overlaps(O, q_bytes, V, kv_bytes) ||
-      overlaps(LSE, l_bytes, Q, q_bytes) || overlaps(LSE, l_bytes, K, kv_bytes) ||
-      overlaps(LSE, l_bytes, V, kv_bytes) || overlaps(LSE, l_bytes, O, q_bytes) ||
-      overlaps(O, q_bytes, bias, b_bytes) || overlaps(LSE, l_bytes, bias, b_bytes))
+  if (overlaps(O, o_bytes, Q, q_bytes) || overlaps(O, o_bytes, K, k_bytes) || overlaps(O, o_bytes, V, v_bytes) ||
+      overlaps(LSE, l_bytes, Q, q_bytes) || overlaps(LSE, l_bytes, K, k_bytes) ||
+      overlaps(LSE, l_bytes, V, v_bytes) || overlaps(LSE, l_bytes, O, o_bytes) ||
+      overlaps(O, o_bytes, bias, b_bytes) || overlaps(LSE, l_bytes, bias, b_bytes))
     return FA_ERR_ALIAS;
   if (BH * Nq == 0) return FA_OK;
   const int dev = check_device();
@@ -107,6 +114,7 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
   a.Nq = Nq;
   a.Nk = Nk;
   a.d = d;
+  a.dv = dv;
   a.scale = scale;
   a.causal = causal == 1;
   a.bias = bias;
@@ -122,15 +130,22 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
 extern "C" int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* LSE,
                       int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
                       float scale, void* stream) {
-  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, 0, nullptr, 0, 0, 0, stream);
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, d, scale, 0, nullptr, 0, 0, 0, stream);
 }
 
 extern "C" int fa_fwd_masked(const void* Q, const void* K, const void* V, void* O, float* LSE,
                              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                              int causal, const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
                              int64_t bias_stride_q, void* stream) {
-  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, scale, causal, bias, bias_stride_b, bias_stride_h,
-                             bias_stride_q, stream);
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, d, scale, causal, bias, bias_stride_b,
+                             bias_stride_h, bias_stride_q, stream);
+}
+
+extern "C" int fa_fwd_dv(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal, const float* bias,
+                         int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q, void* stream) {
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, dv, scale, causal, bias, bias_stride_b,
+                             bias_stride_h, bias_stride_q, stream);
 }
 
 extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

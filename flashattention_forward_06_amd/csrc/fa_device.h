@@ -43,13 +43,17 @@ __device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint
 // 4 rows of a band, and the map is one-to-one over 16 rows).  With 128-byte
 // rows (DIM = 64) odd rows start half way round the banks, so row pairs
 // already differ; the XOR acts on row / 2: chunk ^ (4*((row/2) % 2) +
-// (row/4) % 4), which serves both access patterns.
+// (row/4) % 4), which serves both access patterns.  With 384-byte rows
+// (DIM = 192, 24 chunks) odd rows also start half way round; ROW uses
+// chunk ^ ((row/2) % 8), which stays inside the chunk's aligned group of 8
+// (so inside the row) and makes 16 consecutive rows hit 16 distinct groups.
 enum Swz { SWZ_ROW = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
 
 template <int S, int DIM = D>
 __device__ inline uint32_t swz_chunk(uint32_t row, uint32_t ch) {
-  static_assert(DIM == 64 || DIM == 128 || DIM == 256, "head size");
+  static_assert(DIM == 64 || DIM == 128 || DIM == 256 || (DIM == 192 && S == SWZ_ROW), "row width");
   if constexpr (DIM == 64) return ch ^ ((((row >> 1) & 1u) << 2) | ((row >> 2) & 3u));
+  else if constexpr (DIM == 192) return ch ^ ((row >> 1) & 7u);
   else if constexpr (S == SWZ_ROW) return ch ^ (row & 15u);
   else if constexpr (S == SWZ_TR) return ch ^ ((row & 3u) << 2);
   else return ch ^ (((row & 3u) << 2) | ((row >> 2) & 3u));
@@ -77,25 +81,32 @@ __device__ inline float wave_sum_halves(float x) {
 
 // Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane L of a wave
 // writes its 16 bytes at lds_base + 16*L, so each instruction fills 1 KiB of
-// LDS linearly (1024 / (2*DIM) rows).  The swizzle is applied on the source
-// side: the lane that fills physical chunk P of row r loads logical chunk
-// P ^ f(r) (every swizzle is an XOR, its own inverse).  `ROWS` rows starting
-// at global row `row0` (scalar) go to `lds`; every wave issues
-// ROWS*2*DIM/1024/NWAVES instructions.
+// LDS linearly.  The tile is contiguous in memory and in LDS, so byte x of
+// the LDS tile is row x / (2*DIM), physical chunk (x % (2*DIM)) / 16 (a row
+// may straddle two 1 KiB blocks when 2*DIM does not divide 1024).  The
+// swizzle is applied on the source side: the lane that fills physical chunk
+// P of row r loads logical chunk P ^ f(r) (every swizzle is an XOR, its own
+// inverse).  `ROWS` rows starting at global row `row0` (scalar) go to `lds`;
+// every wave issues ROWS*2*DIM/1024/NWAVES instructions.
 template <int ROWS, int S, int DIM = D>
 __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
   constexpr uint32_t RB = 2 * DIM;          // bytes per row
-  constexpr uint32_t CH = DIM / 8;          // chunks per row
-  constexpr uint32_t RPK = 1024 / RB;       // rows per 1 KiB block
-  constexpr uint32_t CH_SHIFT = DIM == 64 ? 3 : (DIM == 128 ? 4 : 5);
   const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * RB);
+  static_assert(ROWS * (int)RB % (1024 * NWAVES) == 0, "tile must be whole 1 KiB blocks per wave");
   constexpr int N_INST = ROWS * (int)RB / 1024 / NWAVES;
-  static_assert(N_INST >= 1, "tile too small for one copy per wave");
 #pragma unroll
   for (int i = 0; i < N_INST; ++i) {
     const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block
-    const uint32_t row = blk * RPK + ((uint32_t)lane >> CH_SHIFT);
-    const uint32_t pos = (uint32_t)lane & (CH - 1u);          // physical chunk in the row
+    uint32_t row, pos;                                       // pos: physical chunk in the row
+    if constexpr ((RB & (RB - 1)) == 0) {
+      // whole rows per block: 1024 / RB rows, RB / 16 lanes per row
+      row = blk * (1024u / RB) + (uint32_t)lane / (RB / 16u);
+      pos = (uint32_t)lane & (RB / 16u - 1u);
+    } else {
+      const uint32_t x = blk * 1024u + 16u * (uint32_t)lane;  // byte of the tile
+      row = x / RB;
+      pos = (x % RB) >> 4;
+    }
     const uint32_t ch = swz_chunk<S, DIM>(row, pos);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (__attribute__((address_space(3))) void*)((lds_char*)lds + blk * 1024u), 16,

@@ -1,8 +1,10 @@
 // fa_fwd_kernel.hip -- gfx950 (CDNA4) fused attention forward kernel.
 //
 // Computes O = softmax_row(scale * Q K^T) V and the per-row log-sum-exp for
-// BF16 Q/K/V with head size 128 ("FlashAttention'ı Anlamak Bölüm 1",
-// section 0.2, score and output equations without the mask term).
+// BF16 Q/K/V ("FlashAttention'ı Anlamak Bölüm 1", section 0.2, score and
+// output equations): Q and K rows of head size d, V and O rows of d_v,
+// (d, d_v) one of (64, 64), (128, 128), (256, 256) and (192, 128).  The
+// headline shape is d = d_v = 128.
 //
 // Work partition (B200 article, section "Kernel işini nasıl
 // bölümlendiriyor"): one workgroup per tile of BR query rows of one
@@ -31,9 +33,9 @@
 //     three tiles: iteration j computes the scores of tile j+2 and P V of
 //     tile j on the MFMAs while the VALU runs the softmax of tile j+1, so
 //     the exponentials overlap the matrix products of the same wave.
-//   * LDS rows are 256 bytes; 16-byte chunks are XOR-swizzled per row so the
-//     K fragment reads (ds_read_b128) and the V transposing reads are free
-//     of bank conflicts (the swizzled shared memory of the 5090 article's
+//   * LDS rows are 2*d (K) and 2*d_v (V) bytes; 16-byte chunks are
+//     XOR-swizzled per row so the K fragment reads (ds_read_b128) and the V
+//     transposing reads are free of bank conflicts (the swizzled shared memory of the 5090 article's
 //     "v2", re-derived for the gfx950 LDS).
 //   * The softmax scale is folded into exp2 as scale*log2(e).  The running
 //     max is only raised when a row's new max exceeds it by more than
@@ -66,13 +68,14 @@ namespace {
 constexpr int BR = 128;         // query rows per workgroup
 // LDS: the Q tile (BR rows, staged once) and K and V tiles of BC keys, two of
 // each (K(j+2), K(j+3), V(j), V(j+1)): 64 KiB at head size 128 and BC = 64,
-// which leaves room for two workgroups per CU.
-constexpr int lds_bytes(int bc, int dim) {
-  return 4 * bc * 2 * dim > BR * 2 * dim ? 4 * bc * 2 * dim : BR * 2 * dim;
+// 80 KiB at (d, d_v) = (192, 128), either way room for two workgroups per
+// CU (160 KiB).
+constexpr int lds_bytes(int bc, int dqk, int dv) {
+  return 2 * bc * 2 * (dqk + dv) > BR * 2 * dqk ? 2 * bc * 2 * (dqk + dv) : BR * 2 * dqk;
 }
 // Waves per SIMD the register budget allows: head size 256 keeps a 32x256
 // fp32 output accumulator (128 registers) per wave and runs one wave.
-constexpr int waves_per_simd(int dim) { return dim == 256 ? 1 : 2; }
+constexpr int waves_per_simd(int dqk, int dv) { return dqk == 256 || dv == 256 ? 1 : 2; }
 constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 
 // One workgroup computes BR query rows of one (batch, head) against all keys.
@@ -83,19 +86,22 @@ constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 //             a q-tile's diagonal are skipped, tiles crossing it are masked
 //   BIAS      an fp32 bias is added to the scaled scores:
 //             bias[b*sb + h*sh + i*sq + j] (element strides)
-template <int DIM, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+//   DQK, DV   head sizes of Q/K and of V/O
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(waves_per_simd(DIM), waves_per_simd(DIM))))
+__attribute__((amdgpu_waves_per_eu(waves_per_simd(DQK, DV), waves_per_simd(DQK, DV))))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
               const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H,
               int Nq, int Nk, int n_qtiles, float c_log2) {
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
-  constexpr int RB = 2 * DIM;                 // bytes per row
-  constexpr int NT = DIM / 16;                // 16-wide k steps over the head size
-  constexpr int NCB = DIM / 32;               // 32-column blocks of the output
-  constexpr int TILE_BYTES = BC * RB;         // one K or V tile
-  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC, DIM)];
+  constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
+  constexpr int RBV = 2 * DV;                 // bytes per V or O row
+  constexpr int NT = DQK / 16;                // 16-wide k steps over the Q/K head size
+  constexpr int NCB = DV / 32;                // 32-column blocks of the output
+  constexpr int K_TILE = BC * RBQ;            // one K tile
+  constexpr int V_TILE = BC * RBV;            // one V tile
+  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC, DQK, DV)];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -113,12 +119,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
 
-  const size_t head_q = (size_t)bh * (size_t)Nq * DIM;
-  const size_t head_k = (size_t)bh * (size_t)Nk * DIM;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q, (uint32_t)Nq * RB);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k, (uint32_t)Nk * RB);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k, (uint32_t)Nk * RB);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + head_q, (uint32_t)Nq * RB);
+  const size_t bhs = (size_t)bh;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + bhs * (size_t)Nq * DQK, (uint32_t)Nq * RBQ);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + bhs * (size_t)Nk * DQK, (uint32_t)Nk * RBQ);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + bhs * (size_t)Nk * DV, (uint32_t)Nk * RBV);
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + bhs * (size_t)Nq * DV, (uint32_t)Nq * RBV);
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n_full = Nk / BC;  // tiles with BC valid keys
@@ -141,9 +146,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       // no row of this q-tile sees any key: O = 0, LSE = -inf
       const int q = q0 + wave * 32 + c;
 #pragma unroll
-      for (int i = 0; i < DIM / 16; ++i)  // this lane's half row: bytes [DIM*h, DIM*h + DIM)
+      for (int i = 0; i < DV / 16; ++i)  // this lane's half row: bytes [DV*h, DV*h + DV)
         __builtin_amdgcn_raw_buffer_store_b128(uintx4{0u, 0u, 0u, 0u}, ro,
-                                               (uint32_t)q * RB + (uint32_t)DIM * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
+                                               (uint32_t)q * RBV + (uint32_t)DV * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
       if (h == 0 && q < Nq) LSE[(size_t)bh * Nq + q] = -__builtin_inff();
       return;
     }
@@ -180,12 +185,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // iteration j computes the scores of tile j+2 and accumulates P V of tile
   // j, so K(j+2) and V(j) are read while K(j+3) and V(j+1) are copied in.
   char* const kbuf0 = smem;
-  char* const vbuf0 = smem + 2 * TILE_BYTES;
-  auto kbuf = [&](int i) FA_INLINE { return kbuf0 + i * TILE_BYTES; };
-  auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * TILE_BYTES; };
+  char* const vbuf0 = smem + 2 * K_TILE;
+  auto kbuf = [&](int i) FA_INLINE { return kbuf0 + i * K_TILE; };
+  auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * V_TILE; };
 
   // ---- prologue: the Q tile through LDS into registers.
-  tile_to_lds<BR, SWZ_ROW, DIM>(rq, q0, smem, wave_u, lane);
+  tile_to_lds<BR, SWZ_ROW, DQK>(rq, q0, smem, wave_u, lane);
   wait_vmem();
   __syncthreads();
   bf16x8 qb[NT];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
@@ -193,12 +198,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint32_t row = wave * 32 + c;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
-      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + swz<SWZ_ROW, DIM>(row, 2 * t + h)));
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
   }
   __syncthreads();  // the Q staging area is reused from here on
-  tile_to_lds<BC, SWZ_ROW, DIM>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DIM>(rk, BC, kbuf(1), wave_u, lane);
-  tile_to_lds<BC, SWZ_TR, DIM>(rv, 0, vbuf(0), wave_u, lane);
+  tile_to_lds<BC, SWZ_ROW, DQK>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DQK>(rk, BC, kbuf(1), wave_u, lane);
+  tile_to_lds<BC, SWZ_TR, DV>(rv, 0, vbuf(0), wave_u, lane);
   floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
   if constexpr (BIAS) {
     load_bias(0, b0);
@@ -221,7 +226,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const uint32_t row = kb * 32 + c;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DIM>(row, 2 * t + h)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[t], s[kb], 0, 0, 0);
       }
     }
@@ -318,9 +323,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const uint32_t r0 = ks4 * 16 + 4 * hh + sub;
         const uint32_t r1 = r0 + 8;
         const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DIM>(r0, ch) + within));
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DV>(r0, ch) + within));
         const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DIM>(r1, ch) + within));
+            (__attribute__((address_space(3))) shortx4*)((lds_char*)vs + swz<SWZ_TR, DV>(r1, ch) + within));
         // move the two 4-element results as whole dwords (no per-element
         // extraction): a = {lo[0..3], hi[0..3]}
         const uintx2 lo2 = __builtin_bit_cast(uintx2, lo);
@@ -353,7 +358,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles > 1) scores(kbuf(1), s1);
   }
   __syncthreads();  // K(0) consumed: K(2) goes into its buffer
-  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DIM>(rk, 2 * BC, kbuf(0), wave_u, lane);
+  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DQK>(rk, 2 * BC, kbuf(0), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
@@ -371,8 +376,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
     constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
-    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DIM>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DIM>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DV>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
     if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
     floatx16 s2[KB];
     if constexpr (HAS_S2) scores(kbuf(P), s2);
@@ -463,7 +468,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         w0 = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
         w1 = (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16);
       }
-      __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, ro, (uint32_t)q * RB + d * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(uintx2{w0, w1}, ro, (uint32_t)q * RBV + d * 2, 0, 0);
     }
   if (h == 0 && q < Nq) {
     const float ln2 = 0.69314718055994530942f;
@@ -471,21 +476,23 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 }
 
-template <int DIM, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
 const void* kernel_ptr() {
-  return (const void*)&fa_fwd_kernel<DIM, BC, NEG_SCALE, CAUSAL, BIAS>;
+  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS>;
 }
 
-// Kernel for one head size: BC = 64 keys per tile (32 at head size 256, and
-// with a bias, whose tiles live in registers).
-template <int DIM>
+// Kernel for one pair of head sizes: BC = 64 keys per tile (32 at head size
+// 256, and with a bias, whose tiles live in registers).
+template <int DQK, int DV>
 const void* select_kernel(bool neg, bool causal, bool bias) {
-  constexpr int BCP = DIM == 256 ? 32 : 64;
+  constexpr int BCP = DQK == 256 ? 32 : 64;
   // the sign of the scale needs no variant with a bias: the max is taken
   // over the biased logits themselves
-  if (bias) return causal ? kernel_ptr<DIM, 32, false, true, true>() : kernel_ptr<DIM, 32, false, false, true>();
-  if (causal) return neg ? kernel_ptr<DIM, BCP, true, true, false>() : kernel_ptr<DIM, BCP, false, true, false>();
-  return neg ? kernel_ptr<DIM, BCP, true, false, false>() : kernel_ptr<DIM, BCP, false, false, false>();
+  if (bias)
+    return causal ? kernel_ptr<DQK, DV, 32, false, true, true>() : kernel_ptr<DQK, DV, 32, false, false, true>();
+  if (causal)
+    return neg ? kernel_ptr<DQK, DV, BCP, true, true, false>() : kernel_ptr<DQK, DV, BCP, false, true, false>();
+  return neg ? kernel_ptr<DQK, DV, BCP, true, false, false>() : kernel_ptr<DQK, DV, BCP, false, false, false>();
 }
 
 }  // namespace
@@ -507,9 +514,13 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
   float cl = c_log2;
   void* args[] = {&q, &k, &v, &o, &lse, &bias, &sb, &sh, &sq, &heads, &nq, &nk, &nqt, &cl};
   const bool neg = a.scale < 0.0f;
-  const void* fn = a.d == 64    ? select_kernel<64>(neg, a.causal, bias != nullptr)
-                   : a.d == 256 ? select_kernel<256>(neg, a.causal, bias != nullptr)
-                                : select_kernel<128>(neg, a.causal, bias != nullptr);
+  const bool b = bias != nullptr;
+  const void* fn = nullptr;
+  if (a.d == 64 && a.dv == 64) fn = select_kernel<64, 64>(neg, a.causal, b);
+  else if (a.d == 128 && a.dv == 128) fn = select_kernel<128, 128>(neg, a.causal, b);
+  else if (a.d == 256 && a.dv == 256) fn = select_kernel<256, 256>(neg, a.causal, b);
+  else if (a.d == 192 && a.dv == 128) fn = select_kernel<192, 128>(neg, a.causal, b);
+  if (fn == nullptr) return (int)hipErrorInvalidValue;
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }

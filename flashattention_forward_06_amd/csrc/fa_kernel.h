@@ -13,7 +13,8 @@ struct LaunchArgs {
   void* O;
   float* LSE;
   int64_t BH, H, Nq, Nk;
-  int64_t d;            // head size: 64, 128 or 256
+  int64_t d;            // head size of Q and K
+  int64_t dv;           // head size of V and O; (d, dv) in (64, 64), (128, 128), (256, 256), (192, 128)
   float scale;
   bool causal;          // key j hidden from query i when j > i + Nk - Nq
   const float* bias;    // NULL, or fp32 bias[b*bias_sb + h*bias_sh + i*bias_sq + j]

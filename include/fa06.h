@@ -43,7 +43,8 @@ typedef enum fa_status {
     FA_ERR_LAUNCH = 7         /* the kernel launch itself failed                   */
 } fa_status;
 
-/* Head dimension the kernel is built for (d and d_v). */
+/* Head dimension of the headline shape (d = d_v = 128) and the only one the
+ * backward pass (fa_bwd) and the MXFP8 forward (fa_fwd_mxfp8) accept. */
 #define FA_HEAD_DIM 128
 /* Largest Nq or Nk accepted (each per-head slice stays below 2 GiB). */
 #define FA_MAX_SEQ (1LL << 23)
@@ -62,7 +63,8 @@ typedef enum fa_status {
  *   Nq, Nk   query and key/value sequence lengths: Nq >= 0, Nk >= 1 (the
  *            softmax of an empty row is undefined).  Any value up to
  *            FA_MAX_SEQ; no multiple of a tile size is required.
- *   d        head dimension; must equal FA_HEAD_DIM.
+ *   d        head dimension of Q, K, V and O: 64, 128 (FA_HEAD_DIM, the
+ *            tuned case) or 256; anything else returns FA_ERR_UNSUPPORTED.
  *   scale    finite multiplier of Q K^T (1/sqrt(d) for standard attention;
  *            zero and negative values are accepted).
  *   stream   hipStream_t to enqueue on; NULL is the default stream.
@@ -118,6 +120,28 @@ int fa_fwd_masked(const void *Q, const void *K, const void *V, void *O, float *L
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                   int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
                   int64_t bias_stride_q, void *stream);
+
+/*
+ * fa_fwd_dv -- fa_fwd_masked with a value head size d_v that may differ from
+ * the query/key head size d ("FlashAttention'ı Anlamak Bölüm 1", section 0.2
+ * gives V and O their own width d_v; the scale of the score equation divides
+ * by sqrt(d), the query/key width).
+ *
+ *   Q [B, H, Nq, d], K [B, H, Nk, d]   bf16, as for fa_fwd.
+ *   V [B, H, Nk, dv]                    bf16.
+ *   O [B, H, Nq, dv]                    bf16, written.
+ *   d, dv    (d, dv) one of (64, 64), (128, 128), (256, 256) -- the same
+ *            kernels as fa_fwd_masked -- or (192, 128), the query/key and
+ *            value widths of multi-head latent attention's prefill; other
+ *            pairs return FA_ERR_UNSUPPORTED.  Nq and Nk are limited to
+ *            min(FA_MAX_SEQ, 2^30 / max(d, dv)).
+ *   every other argument, ownership, execution and errors as for
+ *   fa_fwd_masked (the alias checks use each buffer's own extent).
+ */
+int fa_fwd_dv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
+              int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+              int64_t bias_stride_q, void *stream);
 
 /*
  * fa_bwd -- gradients of a scalar loss L through the attention output, given

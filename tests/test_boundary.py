@@ -21,7 +21,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_masked", "fa_fwd_mxfp8",
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_dv", "fa_fwd_masked",
+                     "fa_fwd_mxfp8",
                      "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
@@ -181,6 +182,44 @@ def test_other_head_sizes_reach_the_device_check():
         pytest.skip("would launch on fake pointers")
     for d in (64, 128, 256):
         assert call(d=d) == 6
+
+
+# fa_fwd_dv: value head size d_v apart from the query/key head size d
+def call_dv(q=Qp, k=Kp, v=Vp, o=Op, lse=Lp, **kw):
+    a = {**GOOD, "d": 192, "dv": 128, "causal": 0, **kw}
+    return fa.fa_fwd_dv_raw(q, k, v, o, lse, a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dv"], a["scale"],
+                            a["causal"], None, 0, 0, 0, 0)
+
+
+# extents at B=1, H=2, Nq=Nk=256: K (d=192) 196608 bytes, V and O (d_v=128) 131072
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=192, dv=192), 3), (dict(d=128, dv=64), 3), (dict(d=64, dv=128), 3), (dict(d=192, dv=64), 3),
+    (dict(d=256, dv=128), 3), (dict(d=0, dv=0), 3), (dict(causal=2), 3),
+    (dict(Nk=(1 << 30) // 192 + 1), 3), (dict(Nq=(1 << 30) // 192 + 1), 3),
+    (dict(o=0), 1), (dict(v=0), 1), (dict(Nk=0), 2),
+    (dict(v=Vp + 8), 3),
+    (dict(o=Kp + 131072), 4),          # inside K only because K rows are 192 wide
+    (dict(lse=Op + 131068), 4),        # last dword of O (d_v wide)
+    (dict(scale=float("nan")), 5),
+    (dict(Nq=0), 0),
+])
+def test_dv_validation_codes(kw, code):
+    assert call_dv(**kw) == code
+
+
+def test_dv_extents_use_each_buffer_width():
+    # just past K's 192-wide extent and O's 128-wide one: no alias; the
+    # call then fails only at the device check (or launches nothing: Nq=0)
+    assert call_dv(o=Kp + 196608, Nq=0) == 0
+    assert call_dv(lse=Op + 131072, Nq=0) == 0
+    import torch
+    if torch.cuda.is_available():
+        return
+    assert call_dv(o=Kp + 196608) == 6
+    assert call_dv(lse=Op + 131072) == 6
+    for d in (64, 128, 256):
+        assert call_dv(d=d, dv=d) == 6
+    assert call(d=192) == 3   # fa_fwd has d_v = d: (192, 192) has no kernel
 
 
 # MXFP8 entry: fake buffers

@@ -39,11 +39,15 @@ def test_offset_rows_per_head():
 
 def test_workload_table():
     w = fi.WORKLOADS
-    assert [(x.B, x.H, x.Nq, x.Nk, x.d) for x in w.values()] == [
-        (1, 1, 256, 256, 128), (1, 8, 4096, 8192, 128), (4, 16, 4096, 4096, 128),
-        (2, 16, 8192, 8192, 128), (1, 16, 16384, 16384, 128), (2, 32, 8192, 8192, 64),
-        (2, 8, 8192, 8192, 256)]
+    assert [(x.B, x.H, x.Nq, x.Nk, x.d, x.d_v) for x in w.values()] == [
+        (1, 1, 256, 256, 128, 128), (1, 8, 4096, 8192, 128, 128), (4, 16, 4096, 4096, 128, 128),
+        (2, 16, 8192, 8192, 128, 128), (1, 16, 16384, 16384, 128, 128), (2, 32, 8192, 8192, 64, 64),
+        (2, 8, 8192, 8192, 256, 256), (2, 16, 8192, 8192, 192, 128)]
     assert w["rtx5090_q4096_kv8192"].flops == 137438953472
+    # 2 B H Nq Nk (d + d_v): Q K^T over 192, P V over 128
+    assert w["b2_h16_n8192_d192_dv128"].flops == 2 * 2 * 16 * 8192 * 8192 * (192 + 128)
+    Q, K, V = fi.make_workload(fi.Workload("t", 1, 2, 3, 5, d=192, seed=1, dv=128))
+    assert Q.shape == (1, 2, 3, 192) and K.shape == (1, 2, 5, 192) and V.shape == (1, 2, 5, 128)
     assert abs(w["tiny_256"].scale - 0.08838834764831845) < 1e-8
 
 

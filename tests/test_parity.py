@@ -150,7 +150,7 @@ def test_workloads_sampled(fa, name):
         return
     rows = fi.sample_rows(w.B, w.H, w.Nq, 256, seed=w.seed)
     Or, Lr = oracle.attention_rows(Q, K, V, w.scale, rows)
-    og = o.view(-1, w.d)[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
+    og = o.view(-1, w.d_v)[torch.from_numpy(rows).cuda()].float().cpu().numpy().astype(np.float64)
     lg = lse.view(-1)[torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
     check_parity(og, lg, Or, Lr, f"{name} ({len(rows)} sampled rows)")
     # properties over every row: finite, and LSE >= max logit (LSE <= max logit + ln Nk)
