@@ -73,6 +73,9 @@ def parse():
                    help="time the MXFP8 forward (fa_fwd_mxfp8) on the workload's Q, K, V quantized once by the "
                         "library's GPU encoders (not timed); peak = dense FP8 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--splitkv", type=int, default=None, metavar="N",
+                   help="time the key-split forward (fa_fwd_splitkv, split kernel + merge kernel) with N key "
+                        "ranges (0: the library's choice)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="instead of attention, run a plain copy kernel (256 MiB read + 256 MiB "
                         "written per launch) to calibrate the HBM byte counters")
@@ -198,7 +201,17 @@ def main():
         sb, sh, sq = w.H * w.Nk, w.Nk, 0
     if bias is not None and (w.Nk % 4 or bias.data_ptr() % 16):
         raise SystemExit("bias rows must be 16-byte aligned (Nk a multiple of 4)")
-    if w.d_v != w.d:
+    if args.splitkv is not None:
+        if args.mxfp8 or args.bwd:
+            raise SystemExit("--splitkv is a forward option of the bf16 path")
+        ws_bytes, n_used = fa.splitkv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d_v, args.splitkv)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        call = fa.fa_fwd_splitkv_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.d_v, w.scale, int(args.causal),
+                     None if bias is None else bias.data_ptr(), *((sb, sh, sq) if bias is not None else (0, 0, 0)),
+                     args.splitkv, ws.data_ptr(), ws_bytes, sptr)
+    elif w.d_v != w.d:
         call = fa.fa_fwd_dv_raw
         call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                      w.B, w.H, w.Nq, w.Nk, w.d, w.d_v, w.scale, int(args.causal),
@@ -275,7 +288,8 @@ def main():
         "frac": round(achieved / peak, 4),
         "traffic": (MEASURED_TRAFFIC["bytes"]
                     if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
-                        and not args.mxfp8 and bias is None and w.name == MEASURED_TRAFFIC["workload"]) else None),
+                        and not args.mxfp8 and bias is None and args.splitkv is None
+                        and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
     }
     out = {
@@ -293,7 +307,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name + ("+causal" if args.causal else "") +
                    ("" if bias is None else f"+bias_{args.bias}") + ("+bwd" if args.bwd else "") +
-                   ("+mxfp8" if args.mxfp8 else ""), "B": w.B, "H": w.H,
+                   ("+mxfp8" if args.mxfp8 else "") +
+                   ("" if args.splitkv is None else f"+splitkv{n_used}"), "B": w.B, "H": w.H,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "d_v": w.d_v, "causal": bool(args.causal), "bias": args.bias,
                    "flop_per_step": flop, "scale": w.scale, "seed": w.seed,
                    "pct_of_peak": round(100 * value / (MFMA_FP8_PEAK_TFLOPS if args.mxfp8 else MFMA_BF16_PEAK_TFLOPS), 2),
@@ -306,6 +321,8 @@ def main():
         out["bias_bytes"] = bias.numel() * 4
     if args.bwd:
         out["roofline"]["note"] = "whole backward call (delta + dK/dV + dQ kernels); per-kernel split in profiles/"
+    if args.splitkv is not None:
+        out["roofline"]["note"] = f"whole key-split call: split kernel ({n_used} key ranges) + merge kernel"
     if not args.no_cpu_baseline and bias is None and not args.bwd and not args.mxfp8:
         cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse, causal=args.causal)
         out["cpu_baseline"] = cb

@@ -25,6 +25,7 @@ FA_MAX_SEQ = 1 << 23
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE", 3: "FA_ERR_UNSUPPORTED",
     4: "FA_ERR_ALIAS", 5: "FA_ERR_INVALID_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH",
+    8: "FA_ERR_WORKSPACE",
 }
 
 
@@ -65,6 +66,11 @@ def load_library(path: str | None = None):
     lib.fa_fwd_dv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                               ctypes.c_int, vp, i64, i64, i64, vp]
     lib.fa_fwd_dv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                   ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, vp]
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.fa_status_string.argtypes = [ctypes.c_int]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_build_info.argtypes = []
@@ -131,6 +137,26 @@ def fa_fwd_dv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
                                     ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq, stream)
 
 
+def fa_fwd_splitkv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                       B: int, H: int, Nq: int, Nk: int, d: int, dv: int, scale: float, causal: int,
+                       bias_ptr: int | None, sb: int, sh: int, sq: int, n_splits: int,
+                       ws_ptr: int | None, ws_bytes: int, stream: int) -> int:
+    """Direct call of the C ``fa_fwd_splitkv``; returns the status."""
+    return load_library().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
+                                         ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq,
+                                         int(n_splits), ws_ptr, int(ws_bytes), stream)
+
+
+def splitkv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, dv: int, n_splits: int = 0):
+    """(bytes, ranges) of the key-split plan ``fa_fwd_splitkv`` uses for these
+    sizes; raises FaError on invalid sizes."""
+    used = ctypes.c_int64(0)
+    n = load_library().fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, dv, int(n_splits), ctypes.byref(used))
+    if n < 0:
+        raise FaError(-n, fa_status_string(-n))
+    return int(n), int(used.value)
+
+
 def _bias_arg(bias, B: int, H: int, Nq: int, Nk: int, device):
     """Bias tensor -> (tensor kept alive, element strides) in the layout the
     library reads: unit key stride and row/head/batch strides that are
@@ -163,7 +189,8 @@ def _bias_arg(bias, B: int, H: int, Nq: int, Nk: int, device):
     return full, st[0], st[1], st[2]
 
 
-def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False, bias=None):
+def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool = False, bias=None,
+           n_splits: int | None = None, workspace=None):
     """Fused attention forward on torch tensors.
 
     q: [B, H, Nq, d] bf16, k: [B, H, Nk, d], v: [B, H, Nk, dv] bf16, all
@@ -176,6 +203,12 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
     ``(o, lse)``: o [B, H, Nq, dv] bf16 and lse [B, H, Nq] fp32.  Optional
     ``out`` / ``lse`` tensors of those shapes receive the results.  The call is
     enqueued on the current stream of q's device.
+
+    ``n_splits`` (optional) splits every head's keys into ranges computed by
+    separate workgroups and merged (``fa_fwd_splitkv``): 0 lets the library
+    choose, k >= 1 asks for k ranges.  The fp32 workspace it needs is
+    allocated here unless ``workspace`` (a uint8 tensor on q's device of at
+    least ``splitkv_workspace_bytes(...)[0]`` bytes) is given.
     """
     import torch
 
@@ -213,8 +246,22 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
     if bias is not None:
         bias_t, sb, sh, sq = _bias_arg(bias, B, H, Nq, Nk, q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    ws_ptr, ws_bytes = None, 0
+    if n_splits is not None:
+        need, _ = splitkv_workspace_bytes(B, H, Nq, Nk, dv, n_splits)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace is not None:
+            if not isinstance(workspace, torch.Tensor) or workspace.device != q.device or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on q's device")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
-        if dv != d:
+        if n_splits is not None:
+            rc = fa_fwd_splitkv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    B, H, Nq, Nk, d, dv, float(scale), int(bool(causal)),
+                                    None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, int(n_splits),
+                                    ws_ptr, ws_bytes, stream)
+        elif dv != d:
             rc = fa_fwd_dv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                B, H, Nq, Nk, d, dv, float(scale), int(bool(causal)),
                                None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, stream)
@@ -366,4 +413,4 @@ def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, c
 
 
 __all__ = ["fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
-           "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS"]
+           "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes"]

@@ -58,9 +58,42 @@ bool head_sizes_supported(int64_t d, int64_t dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
 
+// Key split of a launch: n_splits ranges of split_keys keys (a multiple of 64,
+// so a range starts on a tile of every kernel variant).  requested = 0 picks
+// enough ranges for the grid to hold at least kSplitTargetWGs workgroups
+// (two per CU), keeping every range at least kSplitMinKeys long; a request
+// above the key count is cut to one range per 64 keys.
+constexpr int64_t kSplitTargetWGs = 512;
+constexpr int64_t kSplitMinKeys = 512;
+constexpr int64_t kSplitMax = 1024;
+
+struct SplitPlan {
+  int64_t n_splits;
+  int64_t split_keys;
+};
+
+SplitPlan plan_split(int64_t BH, int64_t Nq, int64_t Nk, int64_t requested) {
+  int64_t s = requested;
+  if (s == 0) {
+    const int64_t nblk = BH * ((Nq + 127) / 128);
+    s = nblk >= kSplitTargetWGs || nblk == 0 ? 1 : (kSplitTargetWGs + nblk - 1) / nblk;
+    const int64_t cap = Nk / kSplitMinKeys;
+    s = s < cap ? s : (cap > 1 ? cap : 1);
+  }
+  const int64_t tiles = (Nk + 63) / 64;
+  s = s < tiles ? s : tiles;
+  const int64_t keys = ((Nk + s - 1) / s + 63) / 64 * 64;
+  return SplitPlan{(Nk + keys - 1) / keys, keys};
+}
+
+int64_t split_workspace_bytes(const SplitPlan& p, int64_t BH, int64_t Nq, int64_t dv) {
+  return p.n_splits > 1 ? p.n_splits * BH * Nq * (dv * 4 + 4) : 0;
+}
+
 int validate_and_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
                         int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal,
-                        const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
+                        const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream,
+                        int64_t n_splits = 1, void* workspace = nullptr, int64_t workspace_bytes = 0) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (!head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
   const int64_t dmax = d > dv ? d : dv;
@@ -100,10 +133,34 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
       overlaps(LSE, l_bytes, V, v_bytes) || overlaps(LSE, l_bytes, O, o_bytes) ||
       overlaps(O, o_bytes, bias, b_bytes) || overlaps(LSE, l_bytes, bias, b_bytes))
     return FA_ERR_ALIAS;
+  // key split: the plan, its limits and the caller's workspace
+  if (n_splits < 0 || n_splits > kSplitMax) return FA_ERR_UNSUPPORTED;
+  const SplitPlan plan = plan_split(BH, Nq, Nk, n_splits);
+  if (plan.n_splits > 1) {
+    // fp32 partial rows of one (range, head) slice use 32-bit byte offsets;
+    // the merge grid (rows / 4 blocks at most) and the workspace size fit
+    if (Nq * dv * 4 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    if (BH * Nq > (int64_t(1) << 35)) return FA_ERR_UNSUPPORTED;
+    if (BH * ((Nq + 127) / 128) * plan.n_splits > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  }
+  const int64_t ws_need = split_workspace_bytes(plan, BH, Nq, dv);
+  if (plan.n_splits > 1) {
+    if (workspace == nullptr || workspace_bytes < ws_need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
+    if (overlaps(workspace, ws_need, Q, q_bytes) || overlaps(workspace, ws_need, K, k_bytes) ||
+        overlaps(workspace, ws_need, V, v_bytes) || overlaps(workspace, ws_need, O, o_bytes) ||
+        overlaps(workspace, ws_need, LSE, l_bytes) || overlaps(workspace, ws_need, bias, b_bytes))
+      return FA_ERR_ALIAS;
+  }
   if (BH * Nq == 0) return FA_OK;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
   fa06::LaunchArgs a{};
+  a.n_splits = (int)plan.n_splits;
+  a.split_keys = (int)plan.split_keys;
+  if (plan.n_splits > 1) {
+    a.Opart = static_cast<float*>(workspace);
+    a.Lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.n_splits * BH * Nq * dv * 4);
+  }
   a.Q = Q;
   a.K = K;
   a.V = V;
@@ -146,6 +203,28 @@ extern "C" int fa_fwd_dv(const void* Q, const void* K, const void* V, void* O, f
                          int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q, void* stream) {
   return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, dv, scale, causal, bias, bias_stride_b,
                              bias_stride_h, bias_stride_q, stream);
+}
+
+extern "C" int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t dv,
+                                                  int64_t n_splits, int64_t* n_splits_used) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 1 || dv < 1 || dv > 256) return -FA_ERR_INVALID_SHAPE;
+  if (n_splits < 0 || n_splits > kSplitMax) return -FA_ERR_UNSUPPORTED;
+  if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return -FA_ERR_UNSUPPORTED;
+  if (B > 0 && H > INT64_MAX / B) return -FA_ERR_INVALID_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > (int64_t(1) << 40) / FA_MAX_SEQ) return -FA_ERR_INVALID_SHAPE;
+  const SplitPlan p = plan_split(BH, Nq, Nk, n_splits);
+  if (n_splits_used != nullptr) *n_splits_used = p.n_splits;
+  return split_workspace_bytes(p, BH, Nq, dv);
+}
+
+extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                              int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal,
+                              const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                              int64_t bias_stride_q, int64_t n_splits, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, dv, scale, causal, bias, bias_stride_b,
+                             bias_stride_h, bias_stride_q, stream, n_splits, workspace, workspace_bytes);
 }
 
 extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -317,6 +396,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_INVALID_SCALE: return "FA_ERR_INVALID_SCALE: scale must be finite";
     case FA_ERR_DEVICE: return "FA_ERR_DEVICE: no HIP device, or the current device is not gfx950";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, smaller than fa_fwd_splitkv_workspace_bytes "
+                                  "reports, or not 16-byte aligned";
     default: return "unknown fa_status";
   }
 }

@@ -87,13 +87,19 @@ constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 //   BIAS      an fp32 bias is added to the scaled scores:
 //             bias[b*sb + h*sh + i*sq + j] (element strides)
 //   DQK, DV   head sizes of Q/K and of V/O
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+//   SPLIT     the keys are split into n_splits ranges of split_keys keys (a
+//             multiple of BC); workgroup (head, split, q-tile) attends to its
+//             range only and writes the range's normalised output in fp32
+//             to Opart [n_splits, B*H, Nq, DV] and its log-sum-exp to Lpart
+//             [n_splits, B*H, Nq]; a merge kernel combines the ranges
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(DQK, DV), waves_per_simd(DQK, DV))))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
               const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H,
-              int Nq, int Nk, int n_qtiles, float c_log2) {
+              int Nq, int Nk_all, int n_qtiles, float c_log2, float* __restrict__ Opart,
+              float* __restrict__ Lpart, int split_keys, int n_splits) {
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
   constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
   constexpr int RBV = 2 * DV;                 // bytes per V or O row
@@ -114,16 +120,36 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int nblk = gridDim.x;
   const int nfull = nblk & ~7;
   if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
-  const int bh = bid / n_qtiles;
-  int qt = bid - bh * n_qtiles;
+  int bh, qt, split = 0;
+  if constexpr (SPLIT) {
+    // logical order (head, split, q-tile): the q-tiles of one key range of
+    // one head are consecutive, so they share that range in one XCD's L2
+    const int per_bh = n_splits * n_qtiles;
+    bh = bid / per_bh;
+    const int rem = bid - bh * per_bh;
+    split = rem / n_qtiles;
+    qt = rem - split * n_qtiles;
+  } else {
+    bh = bid / n_qtiles;
+    qt = bid - bh * n_qtiles;
+  }
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
+  // this workgroup's keys: [k0, k0 + Nk) of the head's Nk_all
+  const int k0 = SPLIT ? split * split_keys : 0;
+  const int Nk = SPLIT ? (Nk_all - k0 < split_keys ? Nk_all - k0 : split_keys) : Nk_all;
+  // output rows: the head's O / LSE, or this range's slice of the partials
+  const int BH = SPLIT ? nblk / (n_splits * n_qtiles) : 0;
+  const size_t orow0 = SPLIT ? ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)Nq : (size_t)bh * (size_t)Nq;
 
   const size_t bhs = (size_t)bh;
+  const size_t kv_row0 = bhs * (size_t)Nk_all + (size_t)k0;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + bhs * (size_t)Nq * DQK, (uint32_t)Nq * RBQ);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + bhs * (size_t)Nk * DQK, (uint32_t)Nk * RBQ);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + bhs * (size_t)Nk * DV, (uint32_t)Nk * RBV);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + bhs * (size_t)Nq * DV, (uint32_t)Nq * RBV);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + kv_row0 * DQK, (uint32_t)Nk * RBQ);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + kv_row0 * DV, (uint32_t)Nk * RBV);
+  const __amdgpu_buffer_rsrc_t ro = SPLIT ? make_rsrc(Opart + orow0 * DV, (uint32_t)Nq * (uint32_t)(4 * DV))
+                                          : make_rsrc(O + orow0 * DV, (uint32_t)Nq * RBV);
+  float* const lse_out = SPLIT ? Lpart : LSE;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const int n_full = Nk / BC;  // tiles with BC valid keys
@@ -132,7 +158,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // last key visible to this lane's query row (keys above it are masked)
   int key_lim = Nk - 1;
   if constexpr (CAUSAL) {
-    const int off = Nk - Nq;
+    const int off = Nk_all - k0 - Nq;  // key k0 + j is hidden from query i when j > i + off
     const int q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;
     const int lim_last = q_last + off;  // the q-tile's last row sees keys <= lim_last
     const int lim_first = q0 + off;     // its first row sees keys <= lim_first
@@ -145,11 +171,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles == 0) {
       // no row of this q-tile sees any key: O = 0, LSE = -inf
       const int q = q0 + wave * 32 + c;
+      constexpr uint32_t ORB = SPLIT ? 4 * DV : RBV;  // bytes per output row
 #pragma unroll
-      for (int i = 0; i < DV / 16; ++i)  // this lane's half row: bytes [DV*h, DV*h + DV)
+      for (int i = 0; i < (int)ORB / 32; ++i)  // this lane's half row: bytes [ORB/2*h, ORB/2*(h+1))
         __builtin_amdgcn_raw_buffer_store_b128(uintx4{0u, 0u, 0u, 0u}, ro,
-                                               (uint32_t)q * RBV + (uint32_t)DV * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
-      if (h == 0 && q < Nq) LSE[(size_t)bh * Nq + q] = -__builtin_inff();
+                                               (uint32_t)q * ORB + ORB / 2 * (uint32_t)h + 16u * (uint32_t)i, 0, 0);
+      if (h == 0 && q < Nq) lse_out[orow0 + q] = -__builtin_inff();
       return;
     }
   }
@@ -166,7 +193,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int hd = bh - b * H;
     const int qw0 = q0 + wave * 32;
     const int nrows = Nq - qw0 < 32 ? Nq - qw0 : 32;
-    const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq;
+    const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq + k0;
     const uint32_t bytes = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * bias_sq + Nk) * 4) : 0u;
     rb = make_rsrc(base, bytes);
     bias_voff = (uint32_t)((int64_t)c * bias_sq * 4) + 16u * (uint32_t)h;
@@ -459,6 +486,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = cb * 32 + g4 * 8 + 4 * h;
+      if constexpr (SPLIT) {
+        const floatx4 v{oacc[cb][4 * g4 + 0] * inv_l, oacc[cb][4 * g4 + 1] * inv_l, oacc[cb][4 * g4 + 2] * inv_l,
+                        oacc[cb][4 * g4 + 3] * inv_l};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uintx4, v), ro, (uint32_t)q * (4 * DV) + d * 4, 0, 0);
+        continue;
+      }
       uint32_t w0, w1;
       {
         const __bf16 a0 = (__bf16)(oacc[cb][4 * g4 + 0] * inv_l);
@@ -472,27 +505,80 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   if (h == 0 && q < Nq) {
     const float ln2 = 0.69314718055994530942f;
-    LSE[(size_t)bh * Nq + q] = (CAN_BE_EMPTY && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * ln2;
+    lse_out[orow0 + q] = (CAN_BE_EMPTY && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * ln2;
   }
 }
 
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS>
+// Combines the key ranges of a split launch ("FlashAttention'ı Anlamak
+// Bölüm 1", the online-softmax recurrence of section 0, applied once across
+// ranges): per row, with L_s the ranges' log-sum-exps and O_s their
+// normalised outputs, LSE = ln sum_s exp(L_s) and O = sum_s exp(L_s - LSE) O_s.
+// A range that saw no key has L_s = -inf and weight 0; a row that saw none at
+// all gets O = 0, LSE = -inf.  DV / 4 threads per row, 4 columns each.
+template <int DV>
+__global__ void __launch_bounds__(256)
+fa_fwd_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ Lpart, uint16_t* __restrict__ O,
+                    float* __restrict__ LSE, int64_t rows, int n_splits) {
+  constexpr int TPR = DV / 4;
+  constexpr int RPB = 256 / TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + (int64_t)(threadIdx.x / TPR);
+  const int t = (int)(threadIdx.x % TPR);
+  if (r >= rows) return;
+  float m = -__builtin_inff();
+  for (int s = 0; s < n_splits; ++s) m = fmaxf(m, Lpart[(int64_t)s * rows + r]);
+  uint16_t* const o = O + r * DV + 4 * t;
+  if (m == -__builtin_inff()) {
+    *reinterpret_cast<uintx2*>(o) = uintx2{0u, 0u};
+    if (t == 0) LSE[r] = -__builtin_inff();
+    return;
+  }
+  floatx4 acc{0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  for (int s = 0; s < n_splits; ++s) {
+    const int64_t rs = (int64_t)s * rows + r;
+    const float w = __builtin_amdgcn_exp2f((Lpart[rs] - m) * LOG2E);
+    const floatx4 x = *reinterpret_cast<const floatx4*>(Opart + rs * DV + 4 * t);
+    den += w;
+    acc += w * x;
+  }
+  const float inv = 1.0f / den;
+  const __bf16 a0 = (__bf16)(acc[0] * inv), a1 = (__bf16)(acc[1] * inv);
+  const __bf16 a2 = (__bf16)(acc[2] * inv), a3 = (__bf16)(acc[3] * inv);
+  *reinterpret_cast<uintx2*>(o) =
+      uintx2{(uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16),
+             (uint32_t)__builtin_bit_cast(uint16_t, a2) | ((uint32_t)__builtin_bit_cast(uint16_t, a3) << 16)};
+  if (t == 0) LSE[r] = m + __log2f(den) * 0.69314718055994530942f;
+}
+
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT>
 const void* kernel_ptr() {
-  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS>;
+  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS, SPLIT>;
 }
 
 // Kernel for one pair of head sizes: BC = 64 keys per tile (32 at head size
 // 256, and with a bias, whose tiles live in registers).
-template <int DQK, int DV>
+template <int DQK, int DV, bool SPLIT>
 const void* select_kernel(bool neg, bool causal, bool bias) {
   constexpr int BCP = DQK == 256 ? 32 : 64;
   // the sign of the scale needs no variant with a bias: the max is taken
   // over the biased logits themselves
   if (bias)
-    return causal ? kernel_ptr<DQK, DV, 32, false, true, true>() : kernel_ptr<DQK, DV, 32, false, false, true>();
+    return causal ? kernel_ptr<DQK, DV, 32, false, true, true, SPLIT>()
+                  : kernel_ptr<DQK, DV, 32, false, false, true, SPLIT>();
   if (causal)
-    return neg ? kernel_ptr<DQK, DV, BCP, true, true, false>() : kernel_ptr<DQK, DV, BCP, false, true, false>();
-  return neg ? kernel_ptr<DQK, DV, BCP, true, false, false>() : kernel_ptr<DQK, DV, BCP, false, false, false>();
+    return neg ? kernel_ptr<DQK, DV, BCP, true, true, false, SPLIT>()
+               : kernel_ptr<DQK, DV, BCP, false, true, false, SPLIT>();
+  return neg ? kernel_ptr<DQK, DV, BCP, true, false, false, SPLIT>()
+             : kernel_ptr<DQK, DV, BCP, false, false, false, SPLIT>();
+}
+
+template <bool SPLIT>
+const void* select_pair(int64_t d, int64_t dv, bool neg, bool causal, bool bias) {
+  if (d == 64 && dv == 64) return select_kernel<64, 64, SPLIT>(neg, causal, bias);
+  if (d == 128 && dv == 128) return select_kernel<128, 128, SPLIT>(neg, causal, bias);
+  if (d == 256 && dv == 256) return select_kernel<256, 256, SPLIT>(neg, causal, bias);
+  if (d == 192 && dv == 128) return select_kernel<192, 128, SPLIT>(neg, causal, bias);
+  return nullptr;
 }
 
 }  // namespace
@@ -512,16 +598,31 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
   int nq = (int)a.Nq, nk = (int)a.Nk;
   int nqt = n_qtiles;
   float cl = c_log2;
-  void* args[] = {&q, &k, &v, &o, &lse, &bias, &sb, &sh, &sq, &heads, &nq, &nk, &nqt, &cl};
+  const bool split = a.n_splits > 1;
+  float* opart = a.Opart;
+  float* lpart = a.Lpart;
+  int split_keys = a.split_keys;
+  int n_splits = split ? a.n_splits : 1;
+  void* args[] = {&q, &k, &v, &o, &lse, &bias, &sb, &sh, &sq, &heads, &nq, &nk, &nqt, &cl,
+                  &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = nullptr;
-  if (a.d == 64 && a.dv == 64) fn = select_kernel<64, 64>(neg, a.causal, b);
-  else if (a.d == 128 && a.dv == 128) fn = select_kernel<128, 128>(neg, a.causal, b);
-  else if (a.d == 256 && a.dv == 256) fn = select_kernel<256, 256>(neg, a.causal, b);
-  else if (a.d == 192 && a.dv == 128) fn = select_kernel<192, 128>(neg, a.causal, b);
+  const void* fn = split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
+                         : select_pair<false>(a.d, a.dv, neg, a.causal, b);
   if (fn == nullptr) return (int)hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)nblk), dim3(NTHREADS), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nblk * n_splits)), dim3(NTHREADS), args, 0, stream);
+  if (e != hipSuccess || !split) return e == hipSuccess ? 0 : (int)e;
+  // merge the key ranges: DV / 4 threads per row
+  const int64_t rows = a.BH * a.Nq;
+  const int rpb = 256 / (int)(a.dv / 4);
+  const void* mfn = a.dv == 64    ? (const void*)&fa_fwd_merge_kernel<64>
+                    : a.dv == 256 ? (const void*)&fa_fwd_merge_kernel<256>
+                                  : (const void*)&fa_fwd_merge_kernel<128>;
+  const float* cop = opart;
+  const float* clp = lpart;
+  int64_t nrows = rows;
+  void* margs[] = {&cop, &clp, &o, &lse, &nrows, &n_splits};
+  e = hipLaunchKernel(mfn, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), margs, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }
 

@@ -19,6 +19,13 @@ struct LaunchArgs {
   bool causal;          // key j hidden from query i when j > i + Nk - Nq
   const float* bias;    // NULL, or fp32 bias[b*bias_sb + h*bias_sh + i*bias_sq + j]
   int64_t bias_sb, bias_sh, bias_sq;
+  // key split (n_splits > 1): ranges of split_keys keys (a multiple of 64),
+  // partial outputs Opart fp32 [n_splits, BH, Nq, dv] and Lpart fp32
+  // [n_splits, BH, Nq], merged into O and LSE by a second kernel
+  int n_splits;
+  int split_keys;
+  float* Opart;
+  float* Lpart;
 };
 
 // Enqueues the kernel; returns 0 or the hipError_t of the launch.

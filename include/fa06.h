@@ -40,7 +40,8 @@ typedef enum fa_status {
     FA_ERR_ALIAS = 4,         /* O or LSE overlaps Q, K, V or each other           */
     FA_ERR_INVALID_SCALE = 5, /* scale is NaN or infinite                          */
     FA_ERR_DEVICE = 6,        /* no HIP device, or the current device is not gfx950 */
-    FA_ERR_LAUNCH = 7         /* the kernel launch itself failed                   */
+    FA_ERR_LAUNCH = 7,        /* the kernel launch itself failed                   */
+    FA_ERR_WORKSPACE = 8      /* fa_fwd_splitkv: workspace NULL, too small or misaligned */
 } fa_status;
 
 /* Head dimension of the headline shape (d = d_v = 128) and the only one the
@@ -142,6 +143,54 @@ int fa_fwd_dv(const void *Q, const void *K, const void *V, void *O, float *LSE,
               int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
               int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
               int64_t bias_stride_q, void *stream);
+
+/*
+ * fa_fwd_splitkv -- fa_fwd_dv with the keys of every (batch, head) split into
+ * ranges that separate workgroups attend to, then merged.  For launches with
+ * few query tiles (short Nq, few heads: fewer than two workgroups per CU),
+ * where one workgroup per query tile leaves the chip idle.  Each range
+ * yields the normalised output O_s and log-sum-exp L_s of its keys alone
+ * (the online softmax of "FlashAttention'ı Anlamak Bölüm 1", section 0, run
+ * on a contiguous part of the keys); a second kernel combines them as that
+ * recurrence combines two blocks: LSE = ln sum_s exp(L_s),
+ * O = sum_s exp(L_s - LSE) O_s.  The result equals fa_fwd_dv's up to
+ * floating-point order (the ranges' outputs stay fp32 until the merge).
+ *
+ *   n_splits         number of key ranges: 0 lets the library choose (enough
+ *                    ranges for 512 workgroups, each range >= 512 keys; 1
+ *                    when the launch is already large), >= 1 asks for that
+ *                    many (cut to one range per 64 keys).  Ranges are equal
+ *                    multiples of 64 keys, the last one shorter.  0..1024,
+ *                    else FA_ERR_UNSUPPORTED.
+ *   workspace        device memory the call may overwrite, 16-byte aligned,
+ *                    of at least fa_fwd_splitkv_workspace_bytes(...) bytes,
+ *                    not overlapping any other buffer (FA_ERR_ALIAS); owned by
+ *                    the caller and free to reuse once the stream has passed
+ *                    the call.  May be NULL when that size is 0 (one range:
+ *                    the call then is fa_fwd_dv).  Otherwise NULL, too small
+ *                    or misaligned returns FA_ERR_WORKSPACE.
+ *   workspace_bytes  its size.
+ *   every other argument, ownership, execution and errors as for fa_fwd_dv;
+ *   with more than one range, Nq * dv * 4 must stay below 2^31 and B*H*Nq
+ *   at most 2^35 (else FA_ERR_UNSUPPORTED).  Two kernels are enqueued.
+ */
+int fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
+                   int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                   int64_t bias_stride_q, int64_t n_splits, void *workspace, int64_t workspace_bytes,
+                   void *stream);
+
+/*
+ * fa_fwd_splitkv_workspace_bytes -- the workspace fa_fwd_splitkv needs for
+ * these sizes and n_splits (same meaning as there): n_splits * B * H * Nq *
+ * (4 * dv + 4) bytes for the ranges' fp32 outputs and log-sum-exps, 0 when
+ * the plan has one range.  Writes the number of ranges the plan uses to
+ * *n_splits_used (may be NULL).  Host-only arithmetic, no HIP call.
+ * Returns a negative fa_status on invalid sizes (B, H, Nq < 0, Nk < 1,
+ * dv outside 1..256, n_splits outside 0..1024, Nq or Nk above FA_MAX_SEQ).
+ */
+int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t dv,
+                                       int64_t n_splits, int64_t *n_splits_used);
 
 /*
  * fa_bwd -- gradients of a scalar loss L through the attention output, given

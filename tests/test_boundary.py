@@ -22,7 +22,7 @@ def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
     assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_dv", "fa_fwd_masked",
-                     "fa_fwd_mxfp8",
+                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
                      "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
@@ -220,6 +220,68 @@ def test_dv_extents_use_each_buffer_width():
     for d in (64, 128, 256):
         assert call_dv(d=d, dv=d) == 6
     assert call(d=192) == 3   # fa_fwd has d_v = d: (192, 192) has no kernel
+
+
+# fa_fwd_splitkv: the key-split plan (host arithmetic) and the workspace rules
+def plan(B, H, Nq, Nk, dv=128, n=0):
+    return fa.splitkv_workspace_bytes(B, H, Nq, Nk, dv, n)
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,n", [
+    (1, 8, 4096, 8192, 0), (2, 16, 8192, 8192, 0), (1, 16, 128, 65536, 0), (1, 1, 1, 1, 0), (1, 1, 5, 100, 0),
+    (1, 2, 300, 1000, 3), (1, 1, 10, 100, 1000), (1, 1, 10, 256, 5), (3, 5, 77, 8191, 7), (1, 1, 1, 1 << 23, 1024),
+])
+def test_split_plan_covers_the_keys(B, H, Nq, Nk, n):
+    nbytes, used = plan(B, H, Nq, Nk, 128, n)
+    assert used >= 1
+    if n:
+        assert used <= n
+    # equal ranges of a multiple of 64 keys, the last one non-empty
+    keys = -(-Nk // used)
+    keys = -(-keys // 64) * 64
+    assert (used - 1) * keys < Nk <= used * keys
+    assert nbytes == (used * B * H * Nq * (4 * 128 + 4) if used > 1 else 0)
+
+
+def test_split_plan_auto_choices():
+    assert plan(1, 8, 4096, 8192)[1] == 2       # 256 q-tiles -> two ranges of 4096 keys
+    assert plan(2, 16, 8192, 8192) == (0, 1)    # 2048 q-tiles: no split
+    assert plan(1, 16, 128, 65536)[1] == 32     # 16 q-tiles -> 32 ranges of 2048 keys
+    assert plan(1, 16, 128, 2048)[1] == 4       # ranges kept >= 512 keys
+    assert plan(1, 1, 1, 1000)[1] == 1
+    assert plan(1, 1, 1, 1000, n=2)[1] == 2     # an explicit request is honoured
+    for bad in [dict(B=-1), dict(Nk=0), dict(n=-1), dict(n=1025), dict(dv=0), dict(dv=512), dict(Nq=(1 << 23) + 1)]:
+        a = {**dict(B=1, H=1, Nq=10, Nk=100, dv=128, n=0), **bad}
+        with pytest.raises(fa.FaError):
+            plan(a["B"], a["H"], a["Nq"], a["Nk"], a["dv"], a["n"])
+
+
+WSp = 0x80000000
+
+
+def call_split(ws=WSp, ws_bytes=1 << 30, n=2, **kw):
+    a = {**GOOD, "dv": GOOD["d"], "causal": 0, **kw}
+    return fa.fa_fwd_splitkv_raw(kw.get("q", Qp), kw.get("k", Kp), kw.get("v", Vp), kw.get("o", Op),
+                                 kw.get("lse", Lp), a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dv"], a["scale"],
+                                 a["causal"], None, 0, 0, 0, n, ws, ws_bytes, 0)
+
+
+def test_split_workspace_rules():
+    need, used = plan(1, 2, 256, 256, 128, 2)
+    assert used == 2 and need == 2 * 2 * 256 * 516
+    assert call_split(ws=0) == 8                    # NULL with two ranges
+    assert call_split(ws_bytes=need - 1) == 8       # too small
+    assert call_split(ws=WSp + 8) == 8              # misaligned
+    assert call_split(ws=Op + 64) == 4              # overlaps O
+    assert call_split(ws=Kp - 16) == 4              # overlaps K
+    assert call_split(n=1025) == 3 and call_split(n=-1) == 3
+    assert call_split(Nq=0) == 0                    # empty problem: no-op
+    import torch
+    if torch.cuda.is_available():
+        return
+    assert call_split(ws_bytes=need) == 6           # valid: reaches the device check
+    assert call_split(ws=0, ws_bytes=0, n=1) == 6   # one range needs no workspace
+    assert call_split(ws=0, ws_bytes=0, n=0) == 6   # auto plan of a 256-key problem: one range
 
 
 # MXFP8 entry: fake buffers
