@@ -238,8 +238,8 @@ def main():
                      o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, vt8.shape[3],
                      ctypes.c_float(w.scale), int(args.causal), sptr)
     if args.bwd:
-        if bias is not None or w.d != 128 or w.d_v != 128:
-            raise SystemExit("--bwd takes no bias and head size 128 only")
+        if w.d != 128 or w.d_v != 128 or args.splitkv is not None:
+            raise SystemExit("--bwd takes head size 128 only and no --splitkv")
         dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d, seed=w.seed + 5000)[0]
         g = up(dO)
         rc = call(*call_args)  # forward once: O and LSE
@@ -249,10 +249,16 @@ def main():
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
         delta = torch.empty_like(lse)
-        call = fa.fa_bwd_raw
-        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
-                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                     w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), sptr)
+        if bias is None:
+            call = fa.fa_bwd_raw
+            call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                         w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), sptr)
+        else:
+            call = fa.fa_bwd_masked_raw
+            call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                         w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), bias.data_ptr(), sb, sh, sq, sptr)
         flop = flop * 5 // 2
 
     def step():

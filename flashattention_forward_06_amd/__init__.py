@@ -78,6 +78,9 @@ def load_library(path: str | None = None):
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                            ctypes.c_int, vp]
     lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
+                                  ctypes.c_int, vp, i64, i64, i64, vp]
+    lib.fa_bwd_masked.restype = ctypes.c_int
     lib.fa_bwd_build_info.argtypes = []
     lib.fa_bwd_build_info.restype = ctypes.c_char_p
     lib.fa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -112,6 +115,16 @@ def fa_bwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_
     """Direct call of the C ``fa_bwd`` on raw device pointers; returns the status."""
     return load_library().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, delta_ptr,
                                  B, H, Nq, Nk, d, ctypes.c_float(scale), int(causal), stream)
+
+
+def fa_bwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int,
+                      dq_ptr: int, dk_ptr: int, dv_ptr: int, delta_ptr: int,
+                      B: int, H: int, Nq: int, Nk: int, d: int, scale: float, causal: int,
+                      bias_ptr: int | None, sb: int, sh: int, sq: int, stream: int) -> int:
+    """Direct call of the C ``fa_bwd_masked`` on raw device pointers; returns the status."""
+    return load_library().fa_bwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr,
+                                        delta_ptr, B, H, Nq, Nk, d, ctypes.c_float(scale), int(causal), bias_ptr,
+                                        sb, sh, sq, stream)
 
 
 def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
@@ -278,14 +291,16 @@ def fa_fwd(q, k, v, scale: float | None = None, out=None, lse=None, causal: bool
 
 
 def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False,
-           dq=None, dk=None, dv=None, delta=None):
+           dq=None, dk=None, dv=None, delta=None, bias=None):
     """Attention backward on torch tensors: gradients of a loss through O.
 
     q, k, v, o, do: bf16 [B, H, N, 128] contiguous on one HIP device (o and
-    lse are the outputs of ``fa_fwd`` for the same q, k, v, scale and causal
-    flag; lse fp32 [B, H, Nq]).  Returns ``(dq, dk, dv)`` in bf16, plus the
-    fp32 ``delta`` workspace [B, H, Nq] (D_i = dO_i . O_i) as a fourth value.
-    Optional output tensors of those shapes are written in place.
+    lse are the outputs of ``fa_fwd`` for the same q, k, v, scale, causal
+    flag and bias; lse fp32 [B, H, Nq]).  ``bias``: the forward's fp32 bias
+    (broadcastable to [B, H, Nq, Nk]); no gradient is formed for it.
+    Returns ``(dq, dk, dv)`` in bf16, plus the fp32 ``delta`` workspace
+    [B, H, Nq] (D_i = dO_i . O_i) as a fourth value.  Optional output tensors
+    of those shapes are written in place.
     """
     import torch
 
@@ -317,10 +332,19 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
     dv = out(dv, (B, H, Nk, d), torch.bfloat16)
     delta = out(delta, (B, H, Nq), torch.float32)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    bias_t, sb, sh, sq = None, 0, 0, 0
+    if bias is not None:
+        bias_t, sb, sh, sq = _bias_arg(bias, B, H, Nq, Nk, q.device)
     with torch.cuda.device(q.device):
-        rc = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                        B, H, Nq, Nk, d, float(scale), int(bool(causal)), stream)
+        if bias_t is not None:
+            rc = fa_bwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                   lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                   B, H, Nq, Nk, d, float(scale), int(bool(causal)), bias_t.data_ptr(), sb, sh, sq,
+                                   stream)
+        else:
+            rc = fa_bwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                            B, H, Nq, Nk, d, float(scale), int(bool(causal)), stream)
     if rc != 0:
         raise FaError(rc, fa_status_string(rc))
     return dq, dk, dv, delta
@@ -412,5 +436,5 @@ def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, c
     return out, lse
 
 
-__all__ = ["fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+__all__ = ["fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes"]

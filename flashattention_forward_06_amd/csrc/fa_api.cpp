@@ -227,9 +227,12 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
                              bias_stride_h, bias_stride_q, stream, n_splits, workspace, workspace_bytes);
 }
 
-extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-                      const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
-                      int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* stream) {
+namespace {
+
+int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                            const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
+                            int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
+                            int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
   if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
@@ -247,6 +250,20 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
       !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4) || !aligned(D, 4))
     return FA_ERR_UNSUPPORTED;
+  // bias: the forward's rules, plus the span of one key column over all
+  // query rows (the dK/dV kernel addresses it with 32-bit byte offsets)
+  int64_t b_bytes = 0;
+  if (bias != nullptr) {
+    if (bias_sb < 0 || bias_sh < 0 || bias_sq < 0) return FA_ERR_UNSUPPORTED;
+    if (!aligned(bias, 16) || bias_sb % 4 != 0 || bias_sh % 4 != 0 || bias_sq % 4 != 0) return FA_ERR_UNSUPPORTED;
+    if (BH * Nq > 0) {
+      const __int128 ext = (__int128)(B - 1) * bias_sb + (__int128)(H - 1) * bias_sh +
+                           (__int128)(Nq - 1) * bias_sq + Nk;
+      if (ext > kBiasMaxExtent) return FA_ERR_INVALID_SHAPE;
+      b_bytes = (int64_t)ext * 4;
+      if ((__int128)(Nq - 1) * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
+    }
+  }
   const int64_t q_bytes = BH * Nq * row_bytes, kv_bytes = BH * Nk * row_bytes, l_bytes = BH * Nq * 4;
   struct Buf {
     const void* p;
@@ -255,6 +272,7 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   const Buf ins[] = {{Q, q_bytes}, {K, kv_bytes}, {V, kv_bytes}, {O, q_bytes}, {dO, q_bytes}, {LSE, l_bytes}};
   const Buf outs[] = {{dQ, q_bytes}, {dK, kv_bytes}, {dV, kv_bytes}, {D, l_bytes}};
   for (const Buf& o : outs) {
+    if (overlaps(o.p, o.n, bias, b_bytes)) return FA_ERR_ALIAS;
     for (const Buf& i : ins)
       if (overlaps(o.p, o.n, i.p, i.n)) return FA_ERR_ALIAS;
     for (const Buf& o2 : outs)
@@ -279,8 +297,30 @@ extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O
   a.Nk = Nk;
   a.scale = scale;
   a.causal = causal == 1;
+  a.H = H;
+  a.bias = bias;
+  a.bias_sb = bias_sb;
+  a.bias_sh = bias_sh;
+  a.bias_sq = bias_sq;
   if (fa06::launch_fa_bwd(a, static_cast<hipStream_t>(stream)) != 0) return FA_ERR_LAUNCH;
   return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                      const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
+                      int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* stream) {
+  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, scale, causal, nullptr, 0, 0,
+                                 0, stream);
+}
+
+extern "C" int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                             const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
+                             int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
+                             int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q, void* stream) {
+  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, scale, causal, bias,
+                                 bias_stride_b, bias_stride_h, bias_stride_q, stream);
 }
 
 // ---------------------------------------------------------------- MXFP8

@@ -28,6 +28,12 @@
 // S and dP are computed in both the dK/dV and the dQ kernel (seven matrix
 // products instead of five) in exchange for no atomic accumulation of dQ.
 // Tiles read both row-wise and transposed use the SWZ_BOTH swizzle.
+// With an additive fp32 bias b (the mask term of the score equation) the
+// logit is scale q_i.k_j + b_ij and P_ij = exp(logit - LSE_i); the gradients
+// above are unchanged (no gradient is formed for b).  The bias is read from
+// memory straight into registers; a row whose LSE is -inf (it saw no key)
+// has its -LSE clamped to a large finite value, so -inf bias entries give
+// P = 0 rather than NaN.
 // Both matrix kernels run one wave per SIMD (their accumulators and
 // register-resident operands need ~350 registers), so all overlap of VALU
 // and MFMA work is inside the wave: each step computes two 32-row (or
@@ -79,14 +85,18 @@ constexpr int KV_TILE = KV_QB * ROW_BYTES;  // one Q or dO tile: 16 KiB
 // LDS: Q[2], dO[2], LSE[2], D[2]
 constexpr int KV_LDS = 4 * KV_TILE + 4 * KV_QB * 4;
 
-template <bool CAUSAL>
+// Largest finite float: the clamp of -LSE * log2(e) for rows that saw no key.
+constexpr float NL_MAX = 3.0e38f;
+
+template <bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ Dl,
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-                   int Nq, int Nk, int n_ktiles, float c_log2, float scale) {
+                   int Nq, int Nk, int n_ktiles, float c_log2, float scale,
+                   const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H) {
   __shared__ __attribute__((aligned(1024))) char smem[KV_LDS];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -124,6 +134,47 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     kb[t] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
     vb[t] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
   }
+
+  // Bias column of this wave's 32 keys over all query rows: lane (c, h)
+  // reads key kw + c of rows 8g + 4h + e of each 32-row sub-block, one dword
+  // per load, the row offset in the scalar offset.  The resource ends at
+  // the wave's last key of row Nq - 1.
+  __amdgpu_buffer_rsrc_t rb = make_rsrc(nullptr, 0u);
+  uint32_t bias_voff = 0;
+  uint32_t bias_row_bytes = 0;
+  if constexpr (BIAS) {
+    const int b = bh / H;
+    const int hd = bh - b * H;
+    // kw_u, not kw: the resource must be provably wave-uniform, or the
+    // compiler wraps every load in a loop over the distinct descriptors
+    const int kw_u = k0 + wave_u * 32;
+    const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + kw_u;
+    const uint32_t bytes = kw_u < Nk ? (uint32_t)(((int64_t)(Nq - 1) * bias_sq + (Nk - kw_u)) * 4) : 0u;
+    rb = make_rsrc(base, bytes);
+    bias_row_bytes = (uint32_t)(bias_sq * 4);
+    bias_voff = (uint32_t)c * 4u + (uint32_t)(4 * h) * bias_row_bytes;
+  }
+  // A bias that does not depend on the row (stride 0 over queries, e.g. a
+  // key padding mask) is one value per lane for the whole kernel.
+  const bool bias_per_key = BIAS && bias_sq == 0;
+  float bias_key = 0.0f;
+  if constexpr (BIAS) {
+    if (bias_per_key) bias_key = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rb, bias_voff, 0, 0));
+  }
+  // bb[r]: bias of row qb*64 + ib*32 + 8(r/4) + 4h + r%4, key kw + c
+  auto load_bias = [&](int qb, int ib, float (&bb)[16]) FA_INLINE {
+    if (bias_per_key) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) bb[r] = bias_key;
+      return;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t row = (uint32_t)(qb * KV_QB + ib * 32 + 8 * (r >> 2) + (r & 3));
+      bb[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          rb, bias_voff, __builtin_amdgcn_readfirstlane(row * bias_row_bytes), 0));
+    }
+  };
 
   // query blocks that see at least one of the workgroup's keys, and the
   // first block in which every (row, key) pair is visible
@@ -166,7 +217,11 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // Causal kernel: one block of 64 query rows as two sub-blocks of 32, in
   // order (the pipelined form needs more registers than a wave has once
   // the masked steps are in the same kernel).
-  auto step_seq = [&](int qb, int st, auto mask_tag) FA_INLINE {
+  // MASK steps hide the pairs above the causal diagonal and, with a bias,
+  // the rows past Nq of a ragged last block (whose zero Q and LSE would
+  // otherwise give P = exp(bias), possibly infinite).
+  // bb2: the step's bias, both sub-blocks (unused without BIAS)
+  auto step_seq = [&](int qb, int st, auto mask_tag, const float (&bb2)[2][16]) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
     const char* qs = qbuf0 + st * KV_TILE;
     const char* ds = dobuf0 + st * KV_TILE;
@@ -174,6 +229,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const char* dls = dbuf0 + st * KV_QB * 4;
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
+      const float (&bb)[16] = bb2[ib];
       floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
       for (int t = 0; t < 8; ++t)
@@ -190,10 +246,16 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * LOG2E));
+          float p;
+          if constexpr (BIAS) {
+            const float nl = fminf(-l4[e] * LOG2E, NL_MAX);
+            p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, __builtin_fmaf(bb[r], LOG2E, nl)));
+          } else {
+            p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, -l4[e] * LOG2E));
+          }
           if constexpr (MASK) {
             const int row = qb * KV_QB + ib * 32 + 8 * g + 4 * h + e;
-            if (key > row + off) p = 0.0f;
+            if ((CAUSAL && key > row + off) || (BIAS && row >= Nq)) p = 0.0f;
           }
           const float dsv = p * (dp[r] - d4[e]);
           pb[r >> 3][r & 7] = (__bf16)p;
@@ -289,12 +351,24 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     const int st = (qb - qb_first) & 1;
     wait_vmem();
     __syncthreads();  // stage st landed for every wave; stage st^1 is free
+    // the step's bias loads go out before the next stage's copies: loads
+    // complete in order, so using the bias then waits for them alone
+    float bb2[2][16];
+    if constexpr (BIAS) {
+      load_bias(qb, 0, bb2[0]);
+      load_bias(qb, 1, bb2[1]);
+    }
     if (qb + 1 < n_qb) stage_in(qb + 1, st ^ 1);
-    if constexpr (CAUSAL) {
-      if (qb < qb_unmasked)
-        step_seq(qb, st, std::true_type{});
+    if constexpr (CAUSAL || BIAS) {
+      // without the causal mask, a bias kernel runs the masked step (rows
+      // past Nq hidden) everywhere: two step variants in one loop make the
+      // compiler spill
+      const bool mask = (CAUSAL && qb < qb_unmasked) || (BIAS && !CAUSAL) ||
+                        (BIAS && qb == n_qb - 1 && Nq % KV_QB != 0);
+      if (mask)
+        step_seq(qb, st, std::true_type{}, bb2);
       else
-        step_seq(qb, st, std::false_type{});
+        step_seq(qb, st, std::false_type{}, bb2);
     } else {
       step(qb, st, std::false_type{});
     }
@@ -313,13 +387,14 @@ constexpr int DQ_BC = 64;     // keys per tile
 constexpr int DQ_TILE = DQ_BC * ROW_BYTES;
 constexpr int DQ_LDS = 4 * DQ_TILE;  // K[2], V[2]
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
-                 int Nq, int Nk, int n_qtiles, float c_log2, float scale) {
+                 int Nq, int Nk, int n_qtiles, float c_log2, float scale,
+                 const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H) {
   __shared__ __attribute__((aligned(1024))) char smem[DQ_LDS];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -371,7 +446,34 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     qb[t] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
     dob[t] = __builtin_bit_cast(bf16x8, buf_load16(rdo, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
   }
-  const float nl2 = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)q * 4u, 0, 0)) * LOG2E;
+  float nl2 = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)q * 4u, 0, 0)) * LOG2E;
+  if constexpr (BIAS) nl2 = fminf(nl2, NL_MAX);
+
+  // Bias rows of this wave's 32 queries (the forward kernel's pattern): per
+  // 32-key block, lane (c, h) loads keys 8g + 4h .. +3 (g = 0..3) of row
+  // q0 + 32*wave + c as four 16-byte loads; the resource ends at the last key
+  // of the wave's last valid row.
+  __amdgpu_buffer_rsrc_t rb = make_rsrc(nullptr, 0u);
+  uint32_t bias_voff = 0;
+  if constexpr (BIAS) {
+    const int b = bh / H;
+    const int hd = bh - b * H;
+    const int qw0 = q0 + wave_u * 32;  // wave-uniform resource (see the dK/dV kernel)
+    const int nrows = Nq - qw0 < 32 ? Nq - qw0 : 32;
+    const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq;
+    const uint32_t bytes = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * bias_sq + Nk) * 4) : 0u;
+    rb = make_rsrc(base, bytes);
+    bias_voff = (uint32_t)((int64_t)c * bias_sq * 4) + 16u * (uint32_t)h;
+  }
+  auto load_bias = [&](int j, floatx4 (&bt)[2][4]) FA_INLINE {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)(DQ_BC * 4));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bt[kb][g] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    rb, bias_voff + (uint32_t)(kb * 128 + g * 32), soff, 0));
+  };
   const float dq_d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)q * 4u, 0, 0));
 
   floatx16 dqacc[4];
@@ -398,11 +500,16 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int t = 0; t < 8; ++t)
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
   };
-  auto dsoft = [&](const floatx16& s, const floatx16& dp, int kb, int lim, auto mask_tag, bf16x8 (&dsb)[2]) FA_INLINE {
+  auto dsoft = [&](const floatx16& s, const floatx16& dp, int kb, int lim, auto mask_tag, const floatx4 (&bk)[4],
+                   bf16x8 (&dsb)[2]) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, nl2));
+      float p;
+      if constexpr (BIAS)
+        p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, __builtin_fmaf(bk[r >> 2][r & 3], LOG2E, nl2)));
+      else
+        p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c_log2, nl2));
       if constexpr (MASK) {
         const int kk = kb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (kk > lim) p = 0.0f;
@@ -418,15 +525,24 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ks, kb * 32 + k2 * 16, cb, lane),
                                                             dsb[k2], dqacc[cb], 0, 0, 0);
   };
+  // bias of the tile being computed (bt) and of the next one (bn, loaded
+  // one tile ahead so its latency hides behind a tile of work)
+  floatx4 bt[2][4], bn[2][4];
+  if constexpr (BIAS) {
+    if (n_tiles > 0) load_bias(0, bt);
+  }
   auto step = [&](int j, int st, auto mask_tag) FA_INLINE {
     const char* ks = kbuf0 + st * DQ_TILE;
     const char* vs = vbuf0 + st * DQ_TILE;
     const int lim = key_lim - j * DQ_BC;
     floatx16 s0, dp0, s1, dp1;
     bf16x8 ds0[2], ds1[2];
+    if constexpr (BIAS) {
+      if (j + 1 < n_tiles) load_bias(j + 1, bn);
+    }
     sdp(ks, vs, 0, s0, dp0);
     sdp(ks, vs, 1, s1, dp1);
-    dsoft(s0, dp0, 0, lim, mask_tag, ds0);
+    dsoft(s0, dp0, 0, lim, mask_tag, bt[0], ds0);
     // 16 MFMAs of S/dP(1), each followed by 6 VALU of the softmax of block 0
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -434,13 +550,19 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
     dq_acc(ks, 0, ds0);
-    dsoft(s1, dp1, 1, lim, mask_tag, ds1);
+    dsoft(s1, dp1, 1, lim, mask_tag, bt[1], ds1);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
     }
     dq_acc(ks, 1, ds1);
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bt[kb][g] = bn[kb][g];
+    }
   };
 
   if (n_tiles > 0) stage_in(0, 0);
@@ -483,19 +605,29 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   const float* dl = a.Dws;
   int nq = (int)a.Nq, nk = (int)a.Nk;
   float cl = c_log2, sc = a.scale;
+  const float* bias = a.bias;
+  int64_t sb = a.bias_sb, sh = a.bias_sh, sq = a.bias_sq;
+  int heads = (int)a.H;
+  const bool has_bias = bias != nullptr;
   {
     int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
     uint16_t* dv = static_cast<uint16_t*>(a.dV);
-    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc};
-    const void* fn = a.causal ? (const void*)&fa_bwd_dkdv_kernel<true> : (const void*)&fa_bwd_dkdv_kernel<false>;
+    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
+    const void* fn = a.causal ? (has_bias ? (const void*)&fa_bwd_dkdv_kernel<true, true>
+                                          : (const void*)&fa_bwd_dkdv_kernel<true, false>)
+                              : (has_bias ? (const void*)&fa_bwd_dkdv_kernel<false, true>
+                                          : (const void*)&fa_bwd_dkdv_kernel<false, false>);
     if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
   }
   if (rows > 0) {
     int n_qt = (int)((a.Nq + DQ_ROWS - 1) / DQ_ROWS);
     uint16_t* dq = static_cast<uint16_t*>(a.dQ);
-    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dq, &nq, &nk, &n_qt, &cl, &sc};
-    const void* fn = a.causal ? (const void*)&fa_bwd_dq_kernel<true> : (const void*)&fa_bwd_dq_kernel<false>;
+    void* args[] = {&q, &k, &v, &g, &lse, &dl, &dq, &nq, &nk, &n_qt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
+    const void* fn = a.causal ? (has_bias ? (const void*)&fa_bwd_dq_kernel<true, true>
+                                          : (const void*)&fa_bwd_dq_kernel<true, false>)
+                              : (has_bias ? (const void*)&fa_bwd_dq_kernel<false, true>
+                                          : (const void*)&fa_bwd_dq_kernel<false, false>);
     if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
   }
   return 0;

@@ -191,7 +191,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if constexpr (BIAS) {
     const int b = bh / H;
     const int hd = bh - b * H;
-    const int qw0 = q0 + wave * 32;
+    // wave_u, not wave: the resource must be provably wave-uniform, or the
+    // compiler wraps every load in a loop over the distinct descriptors
+    const int qw0 = q0 + wave_u * 32;
     const int nrows = Nq - qw0 < 32 ? Nq - qw0 : 32;
     const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq + k0;
     const uint32_t bytes = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * bias_sq + Nk) * 4) : 0u;

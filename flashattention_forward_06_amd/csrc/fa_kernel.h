@@ -47,6 +47,9 @@ struct BwdArgs {
   int64_t BH, Nq, Nk;
   float scale;
   bool causal;
+  int64_t H;
+  const float* bias;    // NULL, or the forward's fp32 bias (same strides)
+  int64_t bias_sb, bias_sh, bias_sq;
 };
 
 // Enqueues the three backward kernels; returns 0 or non-zero if a launch failed.

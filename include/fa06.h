@@ -225,6 +225,31 @@ int fa_bwd(const void *Q, const void *K, const void *V, const void *O, const voi
            int causal, void *stream);
 
 /*
+ * fa_bwd_masked -- fa_bwd for a forward pass that had an additive bias (the
+ * mask term of the score equation, "FlashAttention'ı Anlamak Bölüm 1",
+ * section 0.2): P_ij = exp(scale q_i.k_j + b_ij - LSE_i); the gradient
+ * equations of fa_bwd are otherwise unchanged.  No gradient of the bias is
+ * formed.
+ *
+ *   bias, bias_stride_b, bias_stride_h, bias_stride_q
+ *            the fp32 bias and element strides the forward pass
+ *            (fa_fwd_masked) used, with its rules (16-byte aligned base,
+ *            strides >= 0 and multiples of 4, -inf hides a key; it may alias
+ *            the inputs but not dQ, dK, dV or D: FA_ERR_ALIAS), plus one
+ *            more: (Nq - 1) * bias_stride_q + Nk + 128 <= 2^29 (a key's
+ *            column over all query rows is addressed with 32-bit byte
+ *            offsets), else FA_ERR_UNSUPPORTED.  NULL: the call is fa_bwd.
+ *   A query row that saw no key (LSE = -inf) gets dQ = 0 and adds nothing
+ *   to dK and dV.
+ *   every other argument, ownership, execution and errors as for fa_bwd.
+ */
+int fa_bwd_masked(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                  const float *LSE, void *dQ, void *dK, void *dV, float *D,
+                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                  int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                  int64_t bias_stride_q, void *stream);
+
+/*
  * MXFP8 attention.  The forward pass of fa_fwd_masked (no bias) on inputs in
  * the OCP microscaling format MXFP8: E4M3 elements, and one E8M0 scale byte
  * (value 2^(s-127); s = 255 is NaN) per block of 32 elements along the

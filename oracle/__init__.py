@@ -70,10 +70,12 @@ def _lib():
                                              _p, _p, _p, _p, _p]
         lib.oracle_attn_bwd_fp64.restype = ctypes.c_int
         lib.oracle_attn_bwd_dq_rows_fp64.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
-                                                     ctypes.c_float, ctypes.c_int, _p, _i64, _p]
+                                                     ctypes.c_float, ctypes.c_int, _p, _i64, _i64, _i64,
+                                                     _p, _i64, _p]
         lib.oracle_attn_bwd_dq_rows_fp64.restype = ctypes.c_int
         lib.oracle_attn_bwd_dkdv_keys_fp64.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64,
-                                                       ctypes.c_float, ctypes.c_int, _p, _i64, _p, _p]
+                                                       ctypes.c_float, ctypes.c_int, _p, _i64, _i64, _i64,
+                                                       _p, _i64, _p, _p]
         lib.oracle_attn_bwd_dkdv_keys_fp64.restype = ctypes.c_int
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = ctypes.c_int
@@ -205,32 +207,35 @@ def attention_bwd(Q, K, V, dO, scale: float, causal: bool = False, bias=None):
     return dQ, dK, dV, D, LSE
 
 
-def attention_bwd_dq_rows(Q, K, V, dO, scale: float, rows, causal: bool = False):
+def attention_bwd_dq_rows(Q, K, V, dO, scale: float, rows, causal: bool = False, bias=None):
     """dQ of selected query rows (flat indices into [B*H*Nq]): [n, d] fp64."""
     B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
     Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
     dO = _check_dO(dO, B, H, Nq, dv)
+    bias_ptr, sb, sh, sq, _keep = _bias_view(bias, B, H, Nq, Nk)
     rows = np.ascontiguousarray(rows, dtype=np.int64)
     dQ = np.empty((rows.shape[0], d))
     rc = _lib().oracle_attn_bwd_dq_rows_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
                                              B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
-                                             rows.ctypes.data, rows.shape[0], dQ.ctypes.data)
+                                             bias_ptr, sb, sh, sq, rows.ctypes.data, rows.shape[0], dQ.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_attn_bwd_dq_rows_fp64 failed with code {rc}")
     return dQ
 
 
-def attention_bwd_dkdv_keys(Q, K, V, dO, scale: float, keys, causal: bool = False):
+def attention_bwd_dkdv_keys(Q, K, V, dO, scale: float, keys, causal: bool = False, bias=None):
     """dK and dV of selected keys (flat indices into [B*H*Nk]): ([n, d], [n, dv]) fp64."""
     B, H, Nq, Nk, d, dv = _shapes(Q, K, V)
     Q, K, V = (np.ascontiguousarray(a) for a in (Q, K, V))
     dO = _check_dO(dO, B, H, Nq, dv)
+    bias_ptr, sb, sh, sq, _keep = _bias_view(bias, B, H, Nq, Nk)
     keys = np.ascontiguousarray(keys, dtype=np.int64)
     dK = np.empty((keys.shape[0], d))
     dV = np.empty((keys.shape[0], dv))
     rc = _lib().oracle_attn_bwd_dkdv_keys_fp64(Q.ctypes.data, K.ctypes.data, V.ctypes.data, dO.ctypes.data,
                                                B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(bool(causal)),
-                                               keys.ctypes.data, keys.shape[0], dK.ctypes.data, dV.ctypes.data)
+                                               bias_ptr, sb, sh, sq, keys.ctypes.data, keys.shape[0],
+                                               dK.ctypes.data, dV.ctypes.data)
     if rc != 0:
         raise ValueError(f"oracle_attn_bwd_dkdv_keys_fp64 failed with code {rc}")
     return dK, dV

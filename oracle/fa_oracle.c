@@ -307,10 +307,13 @@ int oracle_attn_bwd_fp64(const uint16_t *Q, const uint16_t *K, const uint16_t *V
     return failed;
 }
 
-/* dQ of selected query rows (flat indices into [B*H*Nq]): dQ [n_rows, d]. */
+/* dQ of selected query rows (flat indices into [B*H*Nq]): dQ [n_rows, d].
+ * bias (may be NULL) as for oracle_attn_bwd_fp64. */
 int oracle_attn_bwd_dq_rows_fp64(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *dO,
                                  int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
-                                 float scale, int causal, const int64_t *rows, int64_t n_rows, double *dQ)
+                                 float scale, int causal, const float *bias,
+                                 int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
+                                 const int64_t *rows, int64_t n_rows, double *dQ)
 {
     if (!bwd_args_ok(Q, K, V, dO, B, H, Nq, Nk, d, dv) || !dQ || n_rows < 0 || (n_rows > 0 && !rows)) return -1;
     const double sigma = (double)scale;
@@ -337,7 +340,8 @@ int oracle_attn_bwd_dq_rows_fp64(const uint16_t *Q, const uint16_t *K, const uin
             const int64_t bh = flat / Nq, i = flat - bh * Nq;
             const uint16_t *Kh = K + bh * Nk * d, *Vh = V + bh * Nk * dv;
             const int64_t n_vis = visible_keys(causal, i, Nq, Nk);
-            if (!row_probs(Q + flat * d, Kh, n_vis, d, sigma, NULL, p, NULL)) continue;
+            const float *bias_row = bias_row_of(bias, bh, H, i, bias_sb, bias_sh, bias_sq);
+            if (!row_probs(Q + flat * d, Kh, n_vis, d, sigma, bias_row, p, NULL)) continue;
             const double Di = row_dp(dO + flat * dv, Vh, n_vis, dv, p, dp);
             for (int64_t j = 0; j < n_vis; ++j) {
                 const double ds = p[j] * (dp[j] - Di);
@@ -356,8 +360,9 @@ int oracle_attn_bwd_dq_rows_fp64(const uint16_t *Q, const uint16_t *K, const uin
  * scattered into the selected keys only. */
 int oracle_attn_bwd_dkdv_keys_fp64(const uint16_t *Q, const uint16_t *K, const uint16_t *V, const uint16_t *dO,
                                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv,
-                                   float scale, int causal, const int64_t *keys, int64_t n_keys,
-                                   double *dK, double *dV)
+                                   float scale, int causal, const float *bias,
+                                   int64_t bias_sb, int64_t bias_sh, int64_t bias_sq,
+                                   const int64_t *keys, int64_t n_keys, double *dK, double *dV)
 {
     if (!bwd_args_ok(Q, K, V, dO, B, H, Nq, Nk, d, dv) || !dK || !dV || n_keys < 0 || (n_keys > 0 && !keys))
         return -1;
@@ -386,7 +391,8 @@ int oracle_attn_bwd_dkdv_keys_fp64(const uint16_t *Q, const uint16_t *K, const u
             for (int64_t i = 0; i < Nq; ++i) {
                 const int64_t row = bh * Nq + i;
                 const int64_t n_vis = visible_keys(causal, i, Nq, Nk);
-                if (!row_probs(Q + row * d, Kh, n_vis, d, sigma, NULL, p, NULL)) continue;
+                const float *bias_row = bias_row_of(bias, bh, H, i, bias_sb, bias_sh, bias_sq);
+                if (!row_probs(Q + row * d, Kh, n_vis, d, sigma, bias_row, p, NULL)) continue;
                 const double Di = row_dp(dO + row * dv, Vh, n_vis, dv, p, dp);
                 for (int64_t r = 0; r < n_keys; ++r) {
                     if (keys[r] / Nk != bh) continue;

@@ -21,7 +21,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_fwd", "fa_fwd_dv", "fa_fwd_masked",
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_bwd_masked", "fa_fwd", "fa_fwd_dv",
+                     "fa_fwd_masked",
                      "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
                      "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
     for n in names:
@@ -166,6 +167,32 @@ def call_bwd(**kw):
 ])
 def test_bwd_validation_codes(kw, code):
     assert call_bwd(**kw) == code
+
+
+BIASp = 0x60000000  # a free slot among the fake buffers
+
+
+def call_bwd_bias(bias=BIASp, sb=0, sh=0, sq=256, **kw):
+    a = {**GOOD_BWD, **kw}
+    return fa.fa_bwd_masked_raw(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"],
+                                a["dl"], a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["scale"], a["causal"], bias,
+                                sb, sh, sq, 0)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sq=-4), 3), (dict(sh=6), 3), (dict(bias=BIASp + 4), 3),
+    (dict(sq=1 << 28), 3),                          # (Nq-1)*sq + Nk beyond 2^29: a key column's span
+    (dict(sb=1 << 58, B=8), 2),                     # extent beyond 2^60 elements
+    (dict(bias=dKp), 4), (dict(bias=Dp - 64), 4),   # overlaps dK / D
+    (dict(bias=Qp), None), (dict(bias=0), None),    # may alias an input; NULL is plain fa_bwd
+])
+def test_bwd_bias_validation_codes(kw, code):
+    import torch
+    if code is None:
+        if torch.cuda.is_available():
+            pytest.skip("would launch on fake pointers")
+        code = 6
+    assert call_bwd_bias(**kw) == code
 
 
 def test_bwd_accepted_arguments_reach_the_device_check():

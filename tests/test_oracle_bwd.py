@@ -163,19 +163,30 @@ def test_invariants(causal):
         assert np.array_equal(a, 2 * b)
 
 
-def test_sampled_entry_points_equal_the_full_backward():
+@pytest.mark.parametrize("bias_kind", [None, "full", "per_key"])
+def test_sampled_entry_points_equal_the_full_backward(bias_kind):
     B, H, Nq, Nk, d = 2, 3, 40, 50, 16
     Q, K, V = fi.make_qkv(B, H, Nq, Nk, d, seed=18)
     dO = fi.make_qkv(B, H, Nq, 1, d, seed=19)[0]
+    rng = np.random.default_rng(22)
+    bias = None
+    if bias_kind == "full":
+        bias = rng.standard_normal((B, H, Nq, Nk)).astype(np.float32)
+        bias[1, 2, :, 30:] = -np.inf
+        bias[0, 1, 5, :] = -np.inf          # a row that sees no key
+    elif bias_kind == "per_key":
+        bias = (3 * rng.standard_normal((1, H, 1, Nk))).astype(np.float32)
     for causal in (False, True):
-        dQ, dK, dV, _, _ = oracle.attention_bwd(Q, K, V, dO, 0.2, causal=causal)
-        rows = np.array([0, 7, 39, 40, 119, 239], dtype=np.int64)
-        assert np.array_equal(oracle.attention_bwd_dq_rows(Q, K, V, dO, 0.2, rows, causal=causal),
+        dQ, dK, dV, _, _ = oracle.attention_bwd(Q, K, V, dO, 0.2, causal=causal, bias=bias)
+        rows = np.array([0, 7, 39, 40, 45, 119, 239], dtype=np.int64)
+        assert np.array_equal(oracle.attention_bwd_dq_rows(Q, K, V, dO, 0.2, rows, causal=causal, bias=bias),
                               dQ.reshape(-1, d)[rows])
         keys = np.array([0, 49, 50, 77, 299, 77], dtype=np.int64)
-        k1, v1 = oracle.attention_bwd_dkdv_keys(Q, K, V, dO, 0.2, keys, causal=causal)
+        k1, v1 = oracle.attention_bwd_dkdv_keys(Q, K, V, dO, 0.2, keys, causal=causal, bias=bias)
         assert np.allclose(k1, dK.reshape(-1, d)[keys], rtol=0, atol=1e-13)
         assert np.allclose(v1, dV.reshape(-1, d)[keys], rtol=0, atol=1e-13)
+        if bias_kind == "full":
+            assert np.all(dQ[0, 1, 5] == 0)
 
 
 def test_bad_arguments():

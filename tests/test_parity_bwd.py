@@ -173,3 +173,82 @@ def test_bwd_workload_sampled(fa, name):
     check_grad("dQ rows", dq.reshape(-1, 128)[rows], rQ, name)
     check_grad("dK keys", dk.reshape(-1, 128)[keys], rK, name)
     check_grad("dV keys", dv.reshape(-1, 128)[keys], rV, name)
+
+
+def make_bias(kind, B, H, Nq, Nk, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "full":
+        b = (2.0 * rng.standard_normal((B, H, Nq, Nk))).astype(np.float32)
+        b[0, 0, :, Nk // 3:] = -np.inf         # head 0 sees only its first third of the keys
+        b[0, -1, 3, :] = -np.inf               # a row that sees no key: dQ = 0, nothing added to dK, dV
+        return b
+    if kind == "per_key_large":
+        # broadcast over rows; large entries: the zero-padded rows of a ragged
+        # last query block would give exp(60) * 0 = inf * 0 without masking.
+        # Two such keys share the probability (one alone would take all of
+        # it and make dS, hence dQ, vanish to rounding level)
+        b = rng.standard_normal((1, H, 1, Nk)).astype(np.float32)
+        b[..., 5] = 60.0
+        b[..., 77] = 60.0
+        return b
+    if kind == "alibi":
+        i = np.arange(Nq)[:, None] + (Nk - Nq)
+        j = np.arange(Nk)[None, :]
+        slopes = 2.0 ** -(np.arange(H) + 1.0)
+        return (-slopes[:, None, None] * np.abs(i - j))[None].astype(np.float32)
+    raise ValueError(kind)
+
+
+BIAS_CASES = [
+    # B, H, Nq, Nk, causal, kind, seed, note
+    (1, 2, 256, 256, False, "full", 320, "dense bias, tile aligned, -inf keys and an empty row"),
+    (2, 2, 200, 333, False, "full", 321, "dense bias, ragged"),
+    (1, 2, 200, 333, True, "full", 322, "dense bias, causal, ragged"),
+    (1, 2, 200, 130, False, "per_key_large", 323, "per-key bias with +60 entries, ragged last query block"),
+    (1, 2, 300, 130, True, "per_key_large", 324, "per-key bias, causal with Nq > Nk"),
+    (1, 4, 640, 640, True, "alibi", 325, "ALiBi-like slopes, causal, several blocks"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,causal,kind,seed,note", BIAS_CASES)
+def test_bwd_bias_full_compare(fa, B, H, Nq, Nk, causal, kind, seed, note):
+    import torch
+    say(f"case bwd bias={kind} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} seed={seed} ({note})")
+    Q, K, V, dO = make_case(B, H, Nq, Nk, seed)
+    bias = make_bias(kind, B, H, Nq, Nk, seed + 1)
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    bt = torch.from_numpy(bias).cuda()
+    o, lse = fa.fa_fwd(q, k, v, scale=SCALE, causal=causal, bias=bt)
+    dq, dk, dv, _ = fa.fa_bwd(q, k, v, o, lse, g, scale=SCALE, causal=causal, bias=bt)
+    torch.cuda.synchronize()
+    got = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    rQ, rK, rV, _, L = oracle.attention_bwd(Q, K, V, dO, SCALE, causal=causal, bias=bias)
+    for name, a, b in (("dQ", got[0], rQ), ("dK", got[1], rK), ("dV", got[2], rV)):
+        check_grad(name, a, b, note)
+    none = np.isneginf(L)
+    assert np.all(got[0][none] == 0)
+
+
+def test_bwd_bias_workload_sampled(fa):
+    import torch
+    w = fi.WORKLOADS["b2_h16_n8192"]
+    say(f"case bwd with a per-key bias [B,H,1,Nk] on {w.name}, causal and not (sampled rows and keys)")
+    Q, K, V = fi.make_workload(w)
+    dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d, seed=w.seed + 5000)[0]
+    bias = (2.0 * np.random.default_rng(w.seed + 2).standard_normal((w.B, w.H, 1, w.Nk))).astype(np.float32)
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    bt = torch.from_numpy(bias).cuda()
+    rng = np.random.default_rng(w.seed + 3)
+    rows = fi.sample_rows(w.B, w.H, w.Nq, 48, seed=w.seed + 4)
+    head = int(rng.integers(w.B * w.H))
+    keys = np.sort(head * w.Nk + rng.choice(w.Nk, size=16, replace=False)).astype(np.int64)
+    keys = np.concatenate([keys, [head * w.Nk, head * w.Nk + w.Nk - 1]]).astype(np.int64)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd(q, k, v, scale=w.scale, causal=causal, bias=bt)
+        dq, dk, dv, _ = fa.fa_bwd(q, k, v, o, lse, g, scale=w.scale, causal=causal, bias=bt)
+        torch.cuda.synchronize()
+        rQ = oracle.attention_bwd_dq_rows(Q, K, V, dO, w.scale, rows, causal=causal, bias=bias)
+        rK, rV = oracle.attention_bwd_dkdv_keys(Q, K, V, dO, w.scale, keys, causal=causal, bias=bias)
+        check_grad("dQ rows", dq.float().cpu().numpy().reshape(-1, 128)[rows], rQ, f"bias causal={causal}")
+        check_grad("dK keys", dk.float().cpu().numpy().reshape(-1, 128)[keys], rK, f"bias causal={causal}")
+        check_grad("dV keys", dv.float().cpu().numpy().reshape(-1, 128)[keys], rV, f"bias causal={causal}")
