@@ -66,9 +66,10 @@ def parse():
                         "(b, h, key), broadcast over the rows ([B, H, 1, Nk]).  Without a bias the "
                         "oracle sample is timed; with one it is skipped")
     p.add_argument("--bwd", action="store_true",
-                   help="time the backward pass (fa_bwd: dQ, dK, dV from dO, with O and LSE from one forward "
-                        "call) instead of the forward; FLOP = 2.5x the forward's (five matrix products; the "
-                        "kernels' recomputation of S and dP in the dQ pass is not counted)")
+                   help="time the backward pass (fa_bwd_dv: dQ, dK, dV from dO, with O and LSE from one "
+                        "forward call) instead of the forward; FLOP = five matrix products, 2*(3d + 2d_v) per "
+                        "visible pair (2.5x the forward's when d_v = d; the kernels' recomputation of S and dP "
+                        "in the dQ pass is not counted)")
     p.add_argument("--mxfp8", action="store_true",
                    help="time the MXFP8 forward (fa_fwd_mxfp8) on the workload's Q, K, V quantized once by the "
                         "library's GPU encoders (not timed); peak = dense FP8 MFMA")
@@ -238,9 +239,9 @@ def main():
                      o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, vt8.shape[3],
                      ctypes.c_float(w.scale), int(args.causal), sptr)
     if args.bwd:
-        if w.d != 128 or w.d_v != 128 or args.splitkv is not None:
-            raise SystemExit("--bwd takes head size 128 only and no --splitkv")
-        dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d, seed=w.seed + 5000)[0]
+        if (w.d, w.d_v) not in ((64, 64), (128, 128), (192, 128)) or args.splitkv is not None:
+            raise SystemExit("--bwd takes (d, d_v) = (64, 64), (128, 128) or (192, 128) and no --splitkv")
+        dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d_v, seed=w.seed + 5000)[0]
         g = up(dO)
         rc = call(*call_args)  # forward once: O and LSE
         if rc != 0:
@@ -249,17 +250,14 @@ def main():
         dk = torch.empty_like(k)
         dv = torch.empty_like(v)
         delta = torch.empty_like(lse)
-        if bias is None:
-            call = fa.fa_bwd_raw
-            call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
-                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                         w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), sptr)
-        else:
-            call = fa.fa_bwd_masked_raw
-            call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
-                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
-                         w.B, w.H, w.Nq, w.Nk, w.d, w.scale, int(args.causal), bias.data_ptr(), sb, sh, sq, sptr)
-        flop = flop * 5 // 2
+        call = fa.fa_bwd_dv_raw
+        call_args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), g.data_ptr(), lse.data_ptr(),
+                     dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                     w.B, w.H, w.Nq, w.Nk, w.d, w.d_v, w.scale, int(args.causal),
+                     None if bias is None else bias.data_ptr(), *((sb, sh, sq) if bias is not None else (0, 0, 0)),
+                     sptr)
+        # the conventional five products: S and dK, dQ over d; dP and dV over d_v
+        flop = 2 * w.B * w.H * (3 * w.d + 2 * w.d_v) * visible_pairs(w.Nq, w.Nk, args.causal)
 
     def step():
         rc = call(*call_args)

@@ -81,6 +81,9 @@ def load_library(path: str | None = None):
     lib.fa_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_float,
                                   ctypes.c_int, vp, i64, i64, i64, vp]
     lib.fa_bwd_masked.restype = ctypes.c_int
+    lib.fa_bwd_dv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                              ctypes.c_int, vp, i64, i64, i64, vp]
+    lib.fa_bwd_dv.restype = ctypes.c_int
     lib.fa_bwd_build_info.argtypes = []
     lib.fa_bwd_build_info.restype = ctypes.c_char_p
     lib.fa_fwd_mxfp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
@@ -125,6 +128,16 @@ def fa_bwd_masked_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: in
     return load_library().fa_bwd_masked(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr,
                                         delta_ptr, B, H, Nq, Nk, d, ctypes.c_float(scale), int(causal), bias_ptr,
                                         sb, sh, sq, stream)
+
+
+def fa_bwd_dv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int,
+                  dq_ptr: int, dk_ptr: int, dv_ptr: int, delta_ptr: int,
+                  B: int, H: int, Nq: int, Nk: int, d: int, dv: int, scale: float, causal: int,
+                  bias_ptr: int | None, sb: int, sh: int, sq: int, stream: int) -> int:
+    """Direct call of the C ``fa_bwd_dv`` on raw device pointers; returns the status."""
+    return load_library().fa_bwd_dv(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr,
+                                    delta_ptr, B, H, Nq, Nk, d, dv, ctypes.c_float(scale), int(causal), bias_ptr,
+                                    sb, sh, sq, stream)
 
 
 def fa_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
@@ -294,7 +307,8 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
            dq=None, dk=None, dv=None, delta=None, bias=None):
     """Attention backward on torch tensors: gradients of a loss through O.
 
-    q, k, v, o, do: bf16 [B, H, N, 128] contiguous on one HIP device (o and
+    q, k: bf16 [B, H, N, d], v, o, do: [B, H, N, dv], contiguous on one HIP
+    device, (d, dv) one of (64, 64), (128, 128), (192, 128) (o and
     lse are the outputs of ``fa_fwd`` for the same q, k, v, scale, causal
     flag and bias; lse fp32 [B, H, Nq]).  ``bias``: the forward's fp32 bias
     (broadcastable to [B, H, Nq, Nk]); no gradient is formed for it.
@@ -311,8 +325,9 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
             raise ValueError(f"{name} must be contiguous on q's HIP device")
     B, H, Nq, d = q.shape
     Nk = k.shape[2]
-    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, d) or tuple(o.shape) != (B, H, Nq, d) \
-            or tuple(do.shape) != (B, H, Nq, d):
+    dvh = v.shape[3]
+    if tuple(k.shape) != (B, H, Nk, d) or tuple(v.shape) != (B, H, Nk, dvh) or tuple(o.shape) != (B, H, Nq, dvh) \
+            or tuple(do.shape) != (B, H, Nq, dvh):
         raise ValueError("shape mismatch among q, k, v, o, do")
     if not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) \
             or not lse.is_contiguous() or lse.device != q.device:
@@ -329,14 +344,19 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
 
     dq = out(dq, (B, H, Nq, d), torch.bfloat16)
     dk = out(dk, (B, H, Nk, d), torch.bfloat16)
-    dv = out(dv, (B, H, Nk, d), torch.bfloat16)
+    dv = out(dv, (B, H, Nk, dvh), torch.bfloat16)
     delta = out(delta, (B, H, Nq), torch.float32)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     bias_t, sb, sh, sq = None, 0, 0, 0
     if bias is not None:
         bias_t, sb, sh, sq = _bias_arg(bias, B, H, Nq, Nk, q.device)
     with torch.cuda.device(q.device):
-        if bias_t is not None:
+        if dvh != d:
+            rc = fa_bwd_dv_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                               B, H, Nq, Nk, d, dvh, float(scale), int(bool(causal)),
+                               None if bias_t is None else bias_t.data_ptr(), sb, sh, sq, stream)
+        elif bias_t is not None:
             rc = fa_bwd_masked_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
                                    B, H, Nq, Nk, d, float(scale), int(bool(causal)), bias_t.data_ptr(), sb, sh, sq,
@@ -436,5 +456,5 @@ def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, c
     return out, lse
 
 
-__all__ = ["fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+__all__ = ["fa_bwd_dv_raw", "fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes"]

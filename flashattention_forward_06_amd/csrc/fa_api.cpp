@@ -229,18 +229,24 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
 
 namespace {
 
+// (d, dv) pairs with backward kernels: the dK/dV kernel keeps K and V rows
+// and both accumulators in registers, which head size 256 exceeds.
+bool bwd_head_sizes_supported(int64_t d, int64_t dv) {
+  return (d == dv && (d == 64 || d == 128)) || (d == 192 && dv == 128);
+}
+
 int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                             const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
-                            int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
-                            int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
+                            int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal,
+                            const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
-  if (d != FA_HEAD_DIM) return FA_ERR_UNSUPPORTED;
-  if (Nq > FA_MAX_SEQ || Nk > FA_MAX_SEQ) return FA_ERR_UNSUPPORTED;
+  if (!bwd_head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
+  const int64_t dmax = d > dv ? d : dv;
+  if (Nq > max_seq(dmax) || Nk > max_seq(dmax)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
-  const int64_t row_bytes = FA_HEAD_DIM * 2;
-  if (BH > (INT64_MAX / row_bytes) / FA_MAX_SEQ) return FA_ERR_INVALID_SHAPE;
+  if (BH > (INT64_MAX / (dmax * 2)) / max_seq(dmax)) return FA_ERR_INVALID_SHAPE;
   const bool has_q = BH * Nq > 0, has_k = BH > 0;
   if ((has_q && (!Q || !O || !dO || !LSE || !dQ || !D)) || (has_k && (!K || !V || !dK || !dV)))
     return FA_ERR_NULL_POINTER;
@@ -264,13 +270,14 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
       if ((__int128)(Nq - 1) * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
     }
   }
-  const int64_t q_bytes = BH * Nq * row_bytes, kv_bytes = BH * Nk * row_bytes, l_bytes = BH * Nq * 4;
+  const int64_t q_bytes = BH * Nq * d * 2, k_bytes = BH * Nk * d * 2, v_bytes = BH * Nk * dv * 2;
+  const int64_t o_bytes = BH * Nq * dv * 2, l_bytes = BH * Nq * 4;
   struct Buf {
     const void* p;
     int64_t n;
   };
-  const Buf ins[] = {{Q, q_bytes}, {K, kv_bytes}, {V, kv_bytes}, {O, q_bytes}, {dO, q_bytes}, {LSE, l_bytes}};
-  const Buf outs[] = {{dQ, q_bytes}, {dK, kv_bytes}, {dV, kv_bytes}, {D, l_bytes}};
+  const Buf ins[] = {{Q, q_bytes}, {K, k_bytes}, {V, v_bytes}, {O, o_bytes}, {dO, o_bytes}, {LSE, l_bytes}};
+  const Buf outs[] = {{dQ, q_bytes}, {dK, k_bytes}, {dV, v_bytes}, {D, l_bytes}};
   for (const Buf& o : outs) {
     if (overlaps(o.p, o.n, bias, b_bytes)) return FA_ERR_ALIAS;
     for (const Buf& i : ins)
@@ -295,6 +302,8 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
   a.BH = BH;
   a.Nq = Nq;
   a.Nk = Nk;
+  a.d = d;
+  a.dv = dv;
   a.scale = scale;
   a.causal = causal == 1;
   a.H = H;
@@ -311,15 +320,23 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
 extern "C" int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                       const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
                       int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, void* stream) {
-  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, scale, causal, nullptr, 0, 0,
-                                 0, stream);
+  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, d, scale, causal, nullptr, 0,
+                                 0, 0, stream);
 }
 
 extern "C" int fa_bwd_masked(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                              const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
                              int64_t Nq, int64_t Nk, int64_t d, float scale, int causal, const float* bias,
                              int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q, void* stream) {
-  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, scale, causal, bias,
+  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, d, scale, causal, bias,
+                                 bias_stride_b, bias_stride_h, bias_stride_q, stream);
+}
+
+extern "C" int fa_bwd_dv(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                         const float* LSE, void* dQ, void* dK, void* dV, float* D, int64_t B, int64_t H,
+                         int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal, const float* bias,
+                         int64_t bias_stride_b, int64_t bias_stride_h, int64_t bias_stride_q, void* stream) {
+  return bwd_validate_and_launch(Q, K, V, O, dO, LSE, dQ, dK, dV, D, B, H, Nq, Nk, d, dv, scale, causal, bias,
                                  bias_stride_b, bias_stride_h, bias_stride_q, stream);
 }
 

@@ -54,18 +54,21 @@ namespace fa06 {
 namespace {
 
 // ---------------------------------------------------------------- delta
-// 16 lanes per row (16 bytes each), 16 rows per 256-thread workgroup,
-// grid-stride over all rows.
+// DV/8 lanes per row (16 bytes each), 256/(DV/8) rows per 256-thread
+// workgroup, grid-stride over all rows.
+template <int DV>
 __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const uint16_t* __restrict__ O,
                                                            const uint16_t* __restrict__ dO,
                                                            float* __restrict__ Dl, int64_t rows) {
-  const int part = threadIdx.x & 15;
-  for (int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); row - (threadIdx.x >> 4) < rows;
-       row += (int64_t)gridDim.x * 16) {
+  constexpr int LPR = DV / 8;   // lanes per row
+  constexpr int RPB = 256 / LPR;
+  const int part = threadIdx.x % LPR;
+  const int sub = threadIdx.x / LPR;
+  for (int64_t row = (int64_t)blockIdx.x * RPB + sub; row - sub < rows; row += (int64_t)gridDim.x * RPB) {
     float acc = 0.0f;
     if (row < rows) {
-      const uintx4 o = *reinterpret_cast<const uintx4*>(O + row * D + part * 8);
-      const uintx4 g = *reinterpret_cast<const uintx4*>(dO + row * D + part * 8);
+      const uintx4 o = *reinterpret_cast<const uintx4*>(O + row * DV + part * 8);
+      const uintx4 g = *reinterpret_cast<const uintx4*>(dO + row * DV + part * 8);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         acc = __builtin_fmaf(__uint_as_float(o[k] << 16), __uint_as_float(g[k] << 16), acc);
@@ -73,7 +76,7 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const uint16_t* __res
       }
     }
 #pragma unroll
-    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
     if (row < rows && part == 0) Dl[row] = acc;
   }
 }
@@ -81,14 +84,14 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(const uint16_t* __res
 // ---------------------------------------------------------------- dK, dV
 constexpr int KV_KEYS = 128;  // keys per workgroup (32 per wave)
 constexpr int KV_QB = 64;     // query rows per step
-constexpr int KV_TILE = KV_QB * ROW_BYTES;  // one Q or dO tile: 16 KiB
-// LDS: Q[2], dO[2], LSE[2], D[2]
-constexpr int KV_LDS = 4 * KV_TILE + 4 * KV_QB * 4;
+// LDS: Q[2] (rows of 2*DQK bytes), dO[2] (2*DV), LSE[2], D[2]: 66.5 KiB at
+// head size 128, 82.5 KiB at (192, 128)
+constexpr int kv_lds(int dqk, int dv) { return 2 * KV_QB * 2 * (dqk + dv) + 4 * KV_QB * 4; }
 
 // Largest finite float: the clamp of -LSE * log2(e) for rows that saw no key.
 constexpr float NL_MAX = 3.0e38f;
 
-template <bool CAUSAL, bool BIAS>
+template <int DQK, int DV, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -97,7 +100,13 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
                    int Nq, int Nk, int n_ktiles, float c_log2, float scale,
                    const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H) {
-  __shared__ __attribute__((aligned(1024))) char smem[KV_LDS];
+  constexpr int RBQ = 2 * DQK;              // bytes per Q, K, dK row
+  constexpr int RBV = 2 * DV;               // bytes per V, O, dO, dV row
+  constexpr int KV_TILE_Q = KV_QB * RBQ;    // one Q tile
+  constexpr int KV_TILE_O = KV_QB * RBV;    // one dO tile
+  constexpr int NTQ = DQK / 16, NTV = DV / 16;   // 16-wide k steps
+  constexpr int NCQ = DQK / 32, NCV = DV / 32;   // 32-column output blocks
+  __shared__ __attribute__((aligned(1024))) char smem[kv_lds(DQK, DV)];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -116,24 +125,25 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 
   const size_t head_q = (size_t)bh * (size_t)Nq;
   const size_t head_k = (size_t)bh * (size_t)Nk;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * D, (uint32_t)Nq * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * DQK, (uint32_t)Nq * RBQ);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * DV, (uint32_t)Nq * RBV);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + head_q, (uint32_t)Nq * 4u);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + head_q, (uint32_t)Nq * 4u);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * D, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * D, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(dK + head_k * D, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(dV + head_k * D, (uint32_t)Nk * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * DQK, (uint32_t)Nk * RBQ);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * DV, (uint32_t)Nk * RBV);
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(dK + head_k * DQK, (uint32_t)Nk * RBQ);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(dV + head_k * DV, (uint32_t)Nk * RBV);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   // K and V rows of this wave's keys as B operands: kb[t] = K[key][16t + 8h .. +7]
   // (keys past Nk read as zero; their results are not stored)
-  bf16x8 kb[8], vb[8];
+  bf16x8 kb[NTQ], vb[NTV];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    kb[t] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
-    vb[t] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)key * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
-  }
+  for (int t = 0; t < NTQ; ++t)
+    kb[t] = __builtin_bit_cast(bf16x8, buf_load16(rk, (uint32_t)key * RBQ + (uint32_t)(2 * t + h) * 16u));
+#pragma unroll
+  for (int t = 0; t < NTV; ++t)
+    vb[t] = __builtin_bit_cast(bf16x8, buf_load16(rv, (uint32_t)key * RBV + (uint32_t)(2 * t + h) * 16u));
 
   // Bias column of this wave's 32 keys over all query rows: lane (c, h)
   // reads key kw + c of rows 8g + 4h + e of each 32-row sub-block, one dword
@@ -191,12 +201,12 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 
   char* const qbuf0 = smem;
-  char* const dobuf0 = smem + 2 * KV_TILE;
-  char* const lbuf0 = smem + 4 * KV_TILE;
+  char* const dobuf0 = smem + 2 * KV_TILE_Q;
+  char* const lbuf0 = dobuf0 + 2 * KV_TILE_O;
   char* const dbuf0 = lbuf0 + 2 * KV_QB * 4;
   auto stage_in = [&](int qb, int st) FA_INLINE {
-    tile_to_lds<KV_QB, SWZ_BOTH>(rq, (uint32_t)(qb * KV_QB), qbuf0 + st * KV_TILE, wave_u, lane);
-    tile_to_lds<KV_QB, SWZ_BOTH>(rdo, (uint32_t)(qb * KV_QB), dobuf0 + st * KV_TILE, wave_u, lane);
+    tile_to_lds<KV_QB, SWZ_BOTH, DQK>(rq, (uint32_t)(qb * KV_QB), qbuf0 + st * KV_TILE_Q, wave_u, lane);
+    tile_to_lds<KV_QB, SWZ_BOTH, DV>(rdo, (uint32_t)(qb * KV_QB), dobuf0 + st * KV_TILE_O, wave_u, lane);
     // 64 floats of LSE and of D: 16 lanes x 16 bytes each
     if (wave_u < 2 && lane < 16) {
       const __amdgpu_buffer_rsrc_t r = wave_u == 0 ? rl : rd;
@@ -207,12 +217,27 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   };
 
-  floatx16 dvacc[4], dkacc[4];
+  floatx16 dvacc[NCV], dkacc[NCQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    dvacc[i] = floatx16{};
-    dkacc[i] = floatx16{};
-  }
+  for (int i = 0; i < NCV; ++i) dvacc[i] = floatx16{};
+#pragma unroll
+  for (int i = 0; i < NCQ; ++i) dkacc[i] = floatx16{};
+
+  // dV^T += dO^T P and dK^T += Q^T dS, the two column-block loops interleaved
+  constexpr int NCMAX = NCQ > NCV ? NCQ : NCV;
+  auto dvdk = [&](const char* qs, const char* ds, int ib, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) FA_INLINE {
+#pragma unroll
+    for (int cb = 0; cb < NCMAX; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (cb < NCV)
+          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read_a<SWZ_BOTH, DV>(ds, ib * 32 + ks * 16, cb, lane), pb[ks], dvacc[cb], 0, 0, 0);
+        if (cb < NCQ)
+          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              tr_read_a<SWZ_BOTH, DQK>(qs, ib * 32 + ks * 16, cb, lane), dsb[ks], dkacc[cb], 0, 0, 0);
+      }
+  };
 
   // Causal kernel: one block of 64 query rows as two sub-blocks of 32, in
   // order (the pipelined form needs more registers than a wave has once
@@ -223,8 +248,8 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // bb2: the step's bias, both sub-blocks (unused without BIAS)
   auto step_seq = [&](int qb, int st, auto mask_tag, const float (&bb2)[2][16]) FA_INLINE {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const char* qs = qbuf0 + st * KV_TILE;
-    const char* ds = dobuf0 + st * KV_TILE;
+    const char* qs = qbuf0 + st * KV_TILE_Q;
+    const char* ds = dobuf0 + st * KV_TILE_O;
     const char* ls = lbuf0 + st * KV_QB * 4;
     const char* dls = dbuf0 + st * KV_QB * 4;
 #pragma unroll
@@ -232,11 +257,13 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       const float (&bb)[16] = bb2[ib];
       floatx16 s = floatx16{}, dp = floatx16{};
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
+      for (int t = 0; t < NTQ; ++t)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DQK>(qs, ib * 32, t, c, h), kb[t], s, 0, 0,
+                                                    0);
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0, 0);
+      for (int t = 0; t < NTV; ++t)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DV>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0,
+                                                     0);
       // accumulator register r holds row ib*32 + 8(r/4) + 4h + r%4 of the block
       bf16x8 pb[2], dsb[2];
 #pragma unroll
@@ -262,15 +289,7 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
           dsb[r >> 3][r & 7] = (__bf16)dsv;
         }
       }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ds, ib * 32 + ks * 16, cb, lane),
-                                                              pb[ks], dvacc[cb], 0, 0, 0);
-          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(qs, ib * 32 + ks * 16, cb, lane),
-                                                              dsb[ks], dkacc[cb], 0, 0, 0);
-        }
+      dvdk(qs, ds, ib, pb, dsb);
     }
   };
 
@@ -281,11 +300,11 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     s = floatx16{};
     dp = floatx16{};
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
+    for (int t = 0; t < NTQ; ++t)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DQK>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0, 0);
+    for (int t = 0; t < NTV; ++t)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DV>(ds, ib * 32, t, c, h), vb[t], dp, 0, 0, 0);
   };
   auto pds = [&](const char* ls, const char* dls, int qb, int ib, const floatx16& s, const floatx16& dp,
                  auto mask_tag, bf16x8 (&pb)[2], bf16x8 (&dsb)[2]) FA_INLINE {
@@ -310,20 +329,9 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       }
     }
   };
-  auto dvdk = [&](const char* qs, const char* ds, int ib, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) FA_INLINE {
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ds, ib * 32 + ks * 16, cb, lane),
-                                                            pb[ks], dvacc[cb], 0, 0, 0);
-        dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(qs, ib * 32 + ks * 16, cb, lane),
-                                                            dsb[ks], dkacc[cb], 0, 0, 0);
-      }
-  };
   auto step = [&](int qb, int st, auto mask_tag) FA_INLINE {
-    const char* qs = qbuf0 + st * KV_TILE;
-    const char* ds = dobuf0 + st * KV_TILE;
+    const char* qs = qbuf0 + st * KV_TILE_Q;
+    const char* ds = dobuf0 + st * KV_TILE_O;
     const char* ls = lbuf0 + st * KV_QB * 4;
     const char* dls = dbuf0 + st * KV_QB * 4;
     floatx16 s0, dp0, s1, dp1;
@@ -332,14 +340,14 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     sdp(qs, ds, 1, s1, dp1);
     pds(ls, dls, qb, 0, s0, dp0, mask_tag, p0, g0);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NTQ + NTV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
     dvdk(qs, ds, 0, p0, g0);
     pds(ls, dls, qb, 1, s1, dp1, mask_tag, p1, g1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 2 * (NCQ + NCV); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
@@ -360,11 +368,12 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
     if (qb + 1 < n_qb) stage_in(qb + 1, st ^ 1);
     if constexpr (CAUSAL || BIAS) {
-      // without the causal mask, a bias kernel runs the masked step (rows
-      // past Nq hidden) everywhere: two step variants in one loop make the
-      // compiler spill
-      const bool mask = (CAUSAL && qb < qb_unmasked) || (BIAS && !CAUSAL) ||
-                        (BIAS && qb == n_qb - 1 && Nq % KV_QB != 0);
+      // Where two step variants in one loop make the compiler spill (a bias
+      // without the causal mask; the causal mask at (d, d_v) = (192, 128)),
+      // every step is the masked one: its masks are exact on every block,
+      // only a compare per element dearer.
+      constexpr bool ALWAYS_MASK = (BIAS && !CAUSAL) || (CAUSAL && DQK + DV > 256);
+      const bool mask = ALWAYS_MASK || (CAUSAL && qb < qb_unmasked) || (BIAS && qb == n_qb - 1 && Nq % KV_QB != 0);
       if (mask)
         step_seq(qb, st, std::true_type{}, bb2);
       else
@@ -375,19 +384,18 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    store_bf16_row_block(rdk, (uint32_t)key, cb, h, dkacc[cb], scale);
-    store_bf16_row_block(rdv, (uint32_t)key, cb, h, dvacc[cb], 1.0f);
-  }
+  for (int cb = 0; cb < NCQ; ++cb) store_bf16_row_block<DQK>(rdk, (uint32_t)key, cb, h, dkacc[cb], scale);
+#pragma unroll
+  for (int cb = 0; cb < NCV; ++cb) store_bf16_row_block<DV>(rdv, (uint32_t)key, cb, h, dvacc[cb], 1.0f);
 }
 
 // ---------------------------------------------------------------- dQ
 constexpr int DQ_ROWS = 128;  // query rows per workgroup (32 per wave)
 constexpr int DQ_BC = 64;     // keys per tile
-constexpr int DQ_TILE = DQ_BC * ROW_BYTES;
-constexpr int DQ_LDS = 4 * DQ_TILE;  // K[2], V[2]
+// LDS: K[2] (rows of 2*DQK bytes), V[2] (2*DV)
+constexpr int dq_lds(int dqk, int dv) { return 2 * DQ_BC * 2 * (dqk + dv); }
 
-template <bool CAUSAL, bool BIAS>
+template <int DQK, int DV, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -395,7 +403,13 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
                  int Nq, int Nk, int n_qtiles, float c_log2, float scale,
                  const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H) {
-  __shared__ __attribute__((aligned(1024))) char smem[DQ_LDS];
+  constexpr int RBQ = 2 * DQK;
+  constexpr int RBV = 2 * DV;
+  constexpr int DQ_TILE_K = DQ_BC * RBQ;
+  constexpr int DQ_TILE_V = DQ_BC * RBV;
+  constexpr int NTQ = DQK / 16, NTV = DV / 16;
+  constexpr int NCQ = DQK / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[dq_lds(DQK, DV)];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -414,13 +428,13 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   const size_t head_q = (size_t)bh * (size_t)Nq;
   const size_t head_k = (size_t)bh * (size_t)Nk;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * D, (uint32_t)Nq * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + head_q * DQK, (uint32_t)Nq * RBQ);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dO + head_q * DV, (uint32_t)Nq * RBV);
   const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + head_q, (uint32_t)Nq * 4u);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dl + head_q, (uint32_t)Nq * 4u);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * D, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * D, (uint32_t)Nk * ROW_BYTES);
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(dQ + head_q * D, (uint32_t)Nq * ROW_BYTES);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + head_k * DQK, (uint32_t)Nk * RBQ);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + head_k * DV, (uint32_t)Nk * RBV);
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(dQ + head_q * DQK, (uint32_t)Nq * RBQ);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
 
   const int n_full = Nk / DQ_BC;
@@ -440,12 +454,13 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
   // Q and dO rows of this lane's query as B operands (rows past Nq read 0)
-  bf16x8 qb[8], dob[8];
+  bf16x8 qb[NTQ], dob[NTV];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    qb[t] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
-    dob[t] = __builtin_bit_cast(bf16x8, buf_load16(rdo, (uint32_t)q * ROW_BYTES + (uint32_t)(2 * t + h) * 16u));
-  }
+  for (int t = 0; t < NTQ; ++t)
+    qb[t] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)q * RBQ + (uint32_t)(2 * t + h) * 16u));
+#pragma unroll
+  for (int t = 0; t < NTV; ++t)
+    dob[t] = __builtin_bit_cast(bf16x8, buf_load16(rdo, (uint32_t)q * RBV + (uint32_t)(2 * t + h) * 16u));
   float nl2 = -__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rl, (uint32_t)q * 4u, 0, 0)) * LOG2E;
   if constexpr (BIAS) nl2 = fminf(nl2, NL_MAX);
 
@@ -476,15 +491,15 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   const float dq_d = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rd, (uint32_t)q * 4u, 0, 0));
 
-  floatx16 dqacc[4];
+  floatx16 dqacc[NCQ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dqacc[i] = floatx16{};
+  for (int i = 0; i < NCQ; ++i) dqacc[i] = floatx16{};
 
   char* const kbuf0 = smem;
-  char* const vbuf0 = smem + 2 * DQ_TILE;
+  char* const vbuf0 = smem + 2 * DQ_TILE_K;
   auto stage_in = [&](int j, int st) FA_INLINE {
-    tile_to_lds<DQ_BC, SWZ_BOTH>(rk, (uint32_t)(j * DQ_BC), kbuf0 + st * DQ_TILE, wave_u, lane);
-    tile_to_lds<DQ_BC, SWZ_ROW>(rv, (uint32_t)(j * DQ_BC), vbuf0 + st * DQ_TILE, wave_u, lane);
+    tile_to_lds<DQ_BC, SWZ_BOTH, DQK>(rk, (uint32_t)(j * DQ_BC), kbuf0 + st * DQ_TILE_K, wave_u, lane);
+    tile_to_lds<DQ_BC, SWZ_ROW, DV>(rv, (uint32_t)(j * DQ_BC), vbuf0 + st * DQ_TILE_V, wave_u, lane);
   };
 
   // One K/V tile as two 32-key blocks, software pipelined inside the wave:
@@ -494,11 +509,11 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     s = floatx16{};
     dp = floatx16{};
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
+    for (int t = 0; t < NTQ; ++t)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DQK>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
+    for (int t = 0; t < NTV; ++t)
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_ROW, DV>(vs, kb * 32, t, c, h), dob[t], dp, 0, 0, 0);
   };
   auto dsoft = [&](const floatx16& s, const floatx16& dp, int kb, int lim, auto mask_tag, const floatx4 (&bk)[4],
                    bf16x8 (&dsb)[2]) FA_INLINE {
@@ -519,45 +534,49 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto dq_acc = [&](const char* ks, int kb, const bf16x8 (&dsb)[2]) FA_INLINE {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < NCQ; ++cb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
-        dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_read_a<SWZ_BOTH>(ks, kb * 32 + k2 * 16, cb, lane),
-                                                            dsb[k2], dqacc[cb], 0, 0, 0);
+        dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            tr_read_a<SWZ_BOTH, DQK>(ks, kb * 32 + k2 * 16, cb, lane), dsb[k2], dqacc[cb], 0, 0, 0);
   };
   // bias of the tile being computed (bt) and of the next one (bn, loaded
-  // one tile ahead so its latency hides behind a tile of work)
+  // one tile ahead so its latency hides behind a tile of work; at (192, 128)
+  // the registers for that are not there, and each tile loads its own)
+  constexpr bool BIAS_AHEAD = DQK + DV <= 256;
   floatx4 bt[2][4], bn[2][4];
-  if constexpr (BIAS) {
+  if constexpr (BIAS && BIAS_AHEAD) {
     if (n_tiles > 0) load_bias(0, bt);
   }
   auto step = [&](int j, int st, auto mask_tag) FA_INLINE {
-    const char* ks = kbuf0 + st * DQ_TILE;
-    const char* vs = vbuf0 + st * DQ_TILE;
+    const char* ks = kbuf0 + st * DQ_TILE_K;
+    const char* vs = vbuf0 + st * DQ_TILE_V;
     const int lim = key_lim - j * DQ_BC;
     floatx16 s0, dp0, s1, dp1;
     bf16x8 ds0[2], ds1[2];
-    if constexpr (BIAS) {
+    if constexpr (BIAS && BIAS_AHEAD) {
       if (j + 1 < n_tiles) load_bias(j + 1, bn);
+    } else if constexpr (BIAS) {
+      load_bias(j, bt);
     }
     sdp(ks, vs, 0, s0, dp0);
     sdp(ks, vs, 1, s1, dp1);
     dsoft(s0, dp0, 0, lim, mask_tag, bt[0], ds0);
-    // 16 MFMAs of S/dP(1), each followed by 6 VALU of the softmax of block 0
+    // the MFMAs of S/dP(1), each followed by 5 VALU of the softmax of block 0
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NTQ + NTV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
     }
     dq_acc(ks, 0, ds0);
     dsoft(s1, dp1, 1, lim, mask_tag, bt[1], ds1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 2 * NCQ; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
     }
     dq_acc(ks, 1, ds1);
-    if constexpr (BIAS) {
+    if constexpr (BIAS && BIAS_AHEAD) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -578,23 +597,52 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) store_bf16_row_block(rdq, (uint32_t)q, cb, h, dqacc[cb], scale);
+  for (int cb = 0; cb < NCQ; ++cb) store_bf16_row_block<DQK>(rdq, (uint32_t)q, cb, h, dqacc[cb], scale);
+}
+
+// Kernels of one (d, d_v) pair.
+struct BwdKernels {
+  const void* delta;
+  int delta_rows_per_block;
+  const void* dkdv[2][2];  // [causal][bias]
+  const void* dq[2][2];
+};
+
+template <int DQK, int DV>
+BwdKernels bwd_kernels() {
+  BwdKernels k;
+  k.delta = (const void*)&fa_bwd_delta_kernel<DV>;
+  k.delta_rows_per_block = 256 / (DV / 8);
+  k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false>;
+  k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true>;
+  k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false>;
+  k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true>;
+  k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false>;
+  k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true>;
+  k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false>;
+  k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true>;
+  return k;
 }
 
 }  // namespace
 
 int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
+  BwdKernels kn;
+  if (a.d == 64 && a.dv == 64) kn = bwd_kernels<64, 64>();
+  else if (a.d == 128 && a.dv == 128) kn = bwd_kernels<128, 128>();
+  else if (a.d == 192 && a.dv == 128) kn = bwd_kernels<192, 128>();
+  else return 1;
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
-    const int64_t want = (rows + 15) / 16;
+    const int64_t rpb = kn.delta_rows_per_block;
+    const int64_t want = (rows + rpb - 1) / rpb;
     const unsigned grid = (unsigned)(want < (1 << 20) ? want : (1 << 20));
     const uint16_t* o = static_cast<const uint16_t*>(a.O);
     const uint16_t* g = static_cast<const uint16_t*>(a.dO);
     float* dl = a.Dws;
     int64_t n = rows;
     void* args[] = {&o, &g, &dl, &n};
-    if (hipLaunchKernel((const void*)&fa_bwd_delta_kernel, dim3(grid), dim3(256), args, 0, stream) != hipSuccess)
-      return 1;
+    if (hipLaunchKernel(kn.delta, dim3(grid), dim3(256), args, 0, stream) != hipSuccess) return 1;
   }
   const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
   const uint16_t* q = static_cast<const uint16_t*>(a.Q);
@@ -608,27 +656,23 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   const float* bias = a.bias;
   int64_t sb = a.bias_sb, sh = a.bias_sh, sq = a.bias_sq;
   int heads = (int)a.H;
-  const bool has_bias = bias != nullptr;
+  const int ci = a.causal ? 1 : 0;
+  const int bi = bias != nullptr ? 1 : 0;
   {
     int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
     uint16_t* dv = static_cast<uint16_t*>(a.dV);
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
-    const void* fn = a.causal ? (has_bias ? (const void*)&fa_bwd_dkdv_kernel<true, true>
-                                          : (const void*)&fa_bwd_dkdv_kernel<true, false>)
-                              : (has_bias ? (const void*)&fa_bwd_dkdv_kernel<false, true>
-                                          : (const void*)&fa_bwd_dkdv_kernel<false, false>);
-    if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
+    if (hipLaunchKernel(kn.dkdv[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+        hipSuccess)
+      return 1;
   }
   if (rows > 0) {
     int n_qt = (int)((a.Nq + DQ_ROWS - 1) / DQ_ROWS);
     uint16_t* dq = static_cast<uint16_t*>(a.dQ);
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dq, &nq, &nk, &n_qt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
-    const void* fn = a.causal ? (has_bias ? (const void*)&fa_bwd_dq_kernel<true, true>
-                                          : (const void*)&fa_bwd_dq_kernel<true, false>)
-                              : (has_bias ? (const void*)&fa_bwd_dq_kernel<false, true>
-                                          : (const void*)&fa_bwd_dq_kernel<false, false>);
-    if (hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) != hipSuccess) return 1;
+    if (hipLaunchKernel(kn.dq[ci][bi], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) != hipSuccess)
+      return 1;
   }
   return 0;
 }

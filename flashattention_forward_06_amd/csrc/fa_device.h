@@ -46,13 +46,15 @@ __device__ inline uintx4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint
 // (row/4) % 4), which serves both access patterns.  With 384-byte rows
 // (DIM = 192, 24 chunks) odd rows also start half way round; ROW uses
 // chunk ^ ((row/2) % 8), which stays inside the chunk's aligned group of 8
-// (so inside the row) and makes 16 consecutive rows hit 16 distinct groups.
+// (so inside the row) and makes 16 consecutive rows hit 16 distinct groups;
+// BOTH uses the 128-byte-row formula, which also keeps a chunk inside its
+// group of 8 and separates the two row pairs of a transposing read.
 enum Swz { SWZ_ROW = 0, SWZ_TR = 1, SWZ_BOTH = 2 };
 
 template <int S, int DIM = D>
 __device__ inline uint32_t swz_chunk(uint32_t row, uint32_t ch) {
-  static_assert(DIM == 64 || DIM == 128 || DIM == 256 || (DIM == 192 && S == SWZ_ROW), "row width");
-  if constexpr (DIM == 64) return ch ^ ((((row >> 1) & 1u) << 2) | ((row >> 2) & 3u));
+  static_assert(DIM == 64 || DIM == 128 || DIM == 256 || (DIM == 192 && S != SWZ_TR), "row width");
+  if constexpr (DIM == 64 || (DIM == 192 && S == SWZ_BOTH)) return ch ^ ((((row >> 1) & 1u) << 2) | ((row >> 2) & 3u));
   else if constexpr (DIM == 192) return ch ^ ((row >> 1) & 7u);
   else if constexpr (S == SWZ_ROW) return ch ^ (row & 15u);
   else if constexpr (S == SWZ_TR) return ch ^ ((row & 3u) << 2);

@@ -45,6 +45,7 @@ struct BwdArgs {
   void* dV;
   float* Dws;           // [BH, Nq] fp32: receives D_i = dO_i . O_i
   int64_t BH, Nq, Nk;
+  int64_t d, dv;        // head sizes: (64, 64), (128, 128) or (192, 128)
   float scale;
   bool causal;
   int64_t H;

@@ -44,8 +44,8 @@ typedef enum fa_status {
     FA_ERR_WORKSPACE = 8      /* fa_fwd_splitkv: workspace NULL, too small or misaligned */
 } fa_status;
 
-/* Head dimension of the headline shape (d = d_v = 128) and the only one the
- * backward pass (fa_bwd) and the MXFP8 forward (fa_fwd_mxfp8) accept. */
+/* Head dimension of the headline shape (d = d_v = 128), and the only one the
+ * MXFP8 forward (fa_fwd_mxfp8) accepts. */
 #define FA_HEAD_DIM 128
 /* Largest Nq or Nk accepted (each per-head slice stays below 2 GiB). */
 #define FA_MAX_SEQ (1LL << 23)
@@ -211,7 +211,10 @@ int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t
  *            accumulated into).
  *   D        device, fp32 [B, H, Nq] workspace owned by the caller; receives
  *            D_i = dO_i . O_i.
- *   B, H, Nq, Nk, d, scale, causal, stream  as for fa_fwd_masked (no bias).
+ *   B, H, Nq, Nk, scale, causal, stream  as for fa_fwd_masked (no bias).
+ *   d        64 or 128 (FA_HEAD_DIM); other values return FA_ERR_UNSUPPORTED
+ *            (256 included: the dK/dV kernel keeps K, V and both
+ *            accumulators in registers, which that size exceeds).
  *
  * Requirements and errors as for fa_fwd; every pointer must be 16-byte
  * aligned except LSE and D (4 bytes); an output (dQ, dK, dV, D) that overlaps
@@ -248,6 +251,21 @@ int fa_bwd_masked(const void *Q, const void *K, const void *V, const void *O, co
                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
                   int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
                   int64_t bias_stride_q, void *stream);
+
+/*
+ * fa_bwd_dv -- fa_bwd_masked for a forward pass with value head size d_v
+ * apart from the query/key head size d (fa_fwd_dv's shapes): Q, K, dQ, dK
+ * [.., d], V, O, dO, dV [.., dv].  (d, dv) is (64, 64), (128, 128) or
+ * (192, 128); other pairs return FA_ERR_UNSUPPORTED.  Nq and Nk are limited
+ * to min(FA_MAX_SEQ, 2^30 / max(d, dv)).  bias may be NULL.  Every other
+ * argument, ownership, execution and errors as for fa_bwd_masked (the alias
+ * checks use each buffer's own extent).
+ */
+int fa_bwd_dv(const void *Q, const void *K, const void *V, const void *O, const void *dO,
+              const float *LSE, void *dQ, void *dK, void *dV, float *D,
+              int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
+              int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+              int64_t bias_stride_q, void *stream);
 
 /*
  * MXFP8 attention.  The forward pass of fa_fwd_masked (no bias) on inputs in

@@ -21,7 +21,8 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = fa.load_library()
     names = declared_functions()
-    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_bwd_masked", "fa_fwd", "fa_fwd_dv",
+    assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_bwd_dv", "fa_bwd_masked", "fa_fwd",
+                     "fa_fwd_dv",
                      "fa_fwd_masked",
                      "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
                      "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
@@ -159,7 +160,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dl=0), 1),
     (dict(B=-1), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2),
-    (dict(d=64), 3), (dict(d=256), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(d=96), 3), (dict(d=256), 3), (dict(d=192), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
     (dict(o=Op2 + 8), 3), (dict(dv=dVp + 4), 3), (dict(dl=Dp + 2), 3),
     (dict(dq=Qp), 4), (dict(dk=Kp + 256), 4), (dict(dv=dKp), 4), (dict(dl=Lp), 4), (dict(dq=dOp + 512), 4),
     (dict(scale=float("nan")), 5),
@@ -193,6 +194,35 @@ def test_bwd_bias_validation_codes(kw, code):
             pytest.skip("would launch on fake pointers")
         code = 6
     assert call_bwd_bias(**kw) == code
+
+
+def call_bwd_dv(hd=192, hdv=128, **kw):
+    """fa_bwd_dv on the fake buffers; hd, hdv are the head sizes (kw keys
+    override GOOD_BWD's pointers and sizes)."""
+    a = {**GOOD_BWD, **kw}
+    return fa.fa_bwd_dv_raw(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["dl"],
+                            a["B"], a["H"], a["Nq"], a["Nk"], hd, hdv, a["scale"], a["causal"], None, 0, 0, 0, 0)
+
+
+# extents at B=1, H=2, Nq=Nk=256: Q, K, dQ, dK (d=192) 196608 bytes; V, O, dO, dV (d_v=128) 131072
+@pytest.mark.parametrize("kw,code", [
+    (dict(hd=192, hdv=192), 3), (dict(hd=256, hdv=256), 3), (dict(hd=128, hdv=64), 3), (dict(hd=256, hdv=128), 3),
+    (dict(Nk=(1 << 30) // 192 + 1), 3),
+    (dict(dq=Kp + 131072), 4),        # inside K only because K rows are 192 wide
+    (dict(dl=dOp + 131068), 4),       # last dword of dO (d_v wide)
+    (dict(Nk=0), 2), (dict(o=0), 1),
+])
+def test_bwd_dv_validation_codes(kw, code):
+    assert call_bwd_dv(**kw) == code
+
+
+def test_bwd_other_head_sizes_reach_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch on fake pointers")
+    assert call_bwd(d=64) == 6
+    assert call_bwd_dv(hd=64, hdv=64) == 6 and call_bwd_dv(hd=128, hdv=128) == 6 and call_bwd_dv() == 6
+    assert call_bwd_dv(dq=Kp + 196608) == 6   # just past K's 192-wide extent: no alias
 
 
 def test_bwd_accepted_arguments_reach_the_device_check():

@@ -252,3 +252,61 @@ def test_bwd_bias_workload_sampled(fa):
         check_grad("dQ rows", dq.float().cpu().numpy().reshape(-1, 128)[rows], rQ, f"bias causal={causal}")
         check_grad("dK keys", dk.float().cpu().numpy().reshape(-1, 128)[keys], rK, f"bias causal={causal}")
         check_grad("dV keys", dv.float().cpu().numpy().reshape(-1, 128)[keys], rV, f"bias causal={causal}")
+
+
+HD_CASES = [
+    # d, d_v, B, H, Nq, Nk, causal, bias kind, seed, note
+    (64, 64, 1, 2, 256, 256, False, None, 340, "head size 64, tile aligned"),
+    (64, 64, 2, 1, 200, 333, True, None, 341, "head size 64, causal, ragged"),
+    (64, 64, 1, 2, 200, 130, False, "per_key_large", 342, "head size 64, per-key bias, ragged"),
+    (192, 128, 1, 2, 256, 256, False, None, 343, "192 / 128, tile aligned"),
+    (192, 128, 2, 1, 200, 333, True, None, 344, "192 / 128, causal, ragged"),
+    (192, 128, 1, 1, 300, 130, True, None, 345, "192 / 128, causal with Nq > Nk"),
+    (192, 128, 1, 2, 200, 333, False, "full", 346, "192 / 128, dense bias with -inf keys and an empty row"),
+    (192, 128, 1, 2, 200, 333, True, "full", 347, "192 / 128, dense bias, causal"),
+    (192, 128, 1, 2, 1, 700, False, None, 348, "192 / 128, one query row"),
+]
+
+
+@pytest.mark.parametrize("d,dv,B,H,Nq,Nk,causal,kind,seed,note", HD_CASES)
+def test_bwd_head_sizes_full_compare(fa, d, dv, B, H, Nq, Nk, causal, kind, seed, note):
+    import torch
+    say(f"case bwd d={d} d_v={dv} B={B} H={H} Nq={Nq} Nk={Nk} causal={causal} bias={kind} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, d, seed=seed, dv=dv)
+    dO = fi.make_qkv(B, H, Nq, 1, dv, seed=seed + 5000)[0]
+    bias = None if kind is None else make_bias(kind, B, H, Nq, Nk, seed + 1)
+    sc = 1.0 / math.sqrt(d)
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    bt = None if bias is None else torch.from_numpy(bias).cuda()
+    o, lse = fa.fa_fwd(q, k, v, scale=sc, causal=causal, bias=bt)
+    dq, dk, dv_, _ = fa.fa_bwd(q, k, v, o, lse, g, scale=sc, causal=causal, bias=bt)
+    torch.cuda.synchronize()
+    assert tuple(dq.shape) == (B, H, Nq, d) and tuple(dv_.shape) == (B, H, Nk, dv)
+    got = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv_)]
+    rQ, rK, rV, _, L = oracle.attention_bwd(Q, K, V, dO, sc, causal=causal, bias=bias)
+    for name, a, b in (("dQ", got[0], rQ), ("dK", got[1], rK), ("dV", got[2], rV)):
+        check_grad(name, a, b, note)
+    assert np.all(got[0][np.isneginf(L)] == 0)
+
+
+@pytest.mark.parametrize("name", ["b2_h32_n8192_d64", "b2_h16_n8192_d192_dv128"])
+def test_bwd_head_size_workloads_sampled(fa, name):
+    import torch
+    w = fi.WORKLOADS[name]
+    say(f"case bwd workload {name} (sampled rows and keys)")
+    Q, K, V = fi.make_workload(w)
+    dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d_v, seed=w.seed + 5000)[0]
+    q, k, v, g = to_dev(Q), to_dev(K), to_dev(V), to_dev(dO)
+    o, lse = fa.fa_fwd(q, k, v, scale=w.scale)
+    dq, dk, dv, _ = fa.fa_bwd(q, k, v, o, lse, g, scale=w.scale)
+    torch.cuda.synchronize()
+    rows = fi.sample_rows(w.B, w.H, w.Nq, 64, seed=w.seed)
+    rQ = oracle.attention_bwd_dq_rows(Q, K, V, dO, w.scale, rows)
+    rng = np.random.default_rng(w.seed + 1)
+    head = int(rng.integers(w.B * w.H))
+    keys = np.sort(head * w.Nk + rng.choice(w.Nk, size=16, replace=False)).astype(np.int64)
+    keys = np.concatenate([keys, [head * w.Nk, head * w.Nk + w.Nk - 1]]).astype(np.int64)
+    rK, rV = oracle.attention_bwd_dkdv_keys(Q, K, V, dO, w.scale, keys)
+    check_grad("dQ rows", dq.float().cpu().numpy().reshape(-1, w.d)[rows], rQ, name)
+    check_grad("dK keys", dk.float().cpu().numpy().reshape(-1, w.d)[keys], rK, name)
+    check_grad("dV keys", dv.float().cpu().numpy().reshape(-1, w.d_v)[keys], rV, name)
