@@ -38,10 +38,15 @@
 //     transposing reads are free of bank conflicts (the swizzled shared memory of the 5090 article's
 //     "v2", re-derived for the gfx950 LDS).
 //   * The softmax scale is folded into exp2 as scale*log2(e).  The running
-//     max is only raised when a row's new max exceeds it by more than
-//     RESCALE_SLACK (in log2 units); otherwise the stale max is kept, which is
-//     exact because the same max enters P, the row sum and the output.  This
-//     removes almost all O rescaling from the loop.
+//     max is only raised when it has to be; otherwise the stale max is kept,
+//     which is exact because the same max enters P, the row sum and the
+//     output.  Tiles without a mask or bias do not even compute their max:
+//     P = exp2(s*scale*log2(e) - m) uses the running max as it stands (bf16 P
+//     has fp32's exponent range), and only when a lane's tile sum exceeds
+//     2^16 (or is inf, as on the first tile) is the tile recomputed with its
+//     max.  Masked and biased tiles raise the max when the tile's exceeds it
+//     by more than RESCALE_SLACK.  This removes almost all O rescaling and
+//     most of the max reductions from the loop.
 //   * Global accesses use buffer resources sized to each (batch, head)
 //     slice: rows past Nq / Nk read as zero and stores past Nq are dropped,
 //     so ragged sequence lengths need no special load or store paths.
@@ -365,6 +370,48 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
+  // Plain tiles: P = exp2(s*c - m_run) with the running max as it stands, no
+  // tile max.  bf16 P has fp32's exponent range, so this is exact as long as
+  // the values stay moderate; a lane whose tile sum exceeds 2^16 (or is inf:
+  // the first tile, m_run = -inf) sets `fix`, and the caller recomputes the
+  // tile with a raised max (slow path, rare).
+  auto softmax_fast = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> bool {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
+        lsum += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    lsum_out = lsum;
+    return __ballot(!(lsum <= 65536.0f)) != 0;
+  };
+  // slow path of a plain tile: raise the max to the tile's, recompute P
+  auto softmax_fix = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> float {
+    float ext = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
+    ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
+    const float m_new = fmaxf(m_run, ext * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_new));
+        lsum += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    lsum_out = lsum;
+    return alpha;
+  };
+
   auto rescale_o = [&](float alpha) FA_INLINE {
 #pragma unroll
     for (int i = 0; i < NCB; ++i)
@@ -413,11 +460,25 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     bf16x8 pn[2 * KB];
     bool rs = false;
     float alpha = 1.0f;
-    if constexpr (HAS_S1) alpha = softmax(s1, bcur, pn, key_lim - (j + 1) * BC, mask1_tag, rs);
+    constexpr bool FAST = !BIAS && !decltype(mask1_tag)::value;
+    float lsum_f = 0.0f;
+    bool fix = false;
+    if constexpr (HAS_S1) {
+      if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f);
+      else alpha = softmax(s1, bcur, pn, key_lim - (j + 1) * BC, mask1_tag, rs);
+    }
     accumulate(vbuf(P), pb);
     if constexpr (HAS_S1) {
 #pragma unroll
       for (int i = 0; i < 2 * KB; ++i) keep(pn[i]);
+      if constexpr (FAST) {
+        keep(lsum_f);
+        if (fix) {
+          alpha = softmax_fix(s1, pn, lsum_f);
+          rs = true;
+        }
+        l_run = l_run * alpha + lsum_f;
+      }
       keep(l_run);
       if (rs) rescale_o(alpha);
 #pragma unroll
@@ -629,9 +690,10 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v4: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+  return "gfx950 fa_fwd v5: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16, "
-         "V^T via ds_read_b64_tr_b16; causal tile skipping; fp32 additive bias";
+         "V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; "
+         "fp32 additive bias; key split with LSE merge";
 }
 
 }  // namespace fa06
