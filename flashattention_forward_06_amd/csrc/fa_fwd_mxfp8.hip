@@ -272,6 +272,58 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     return alpha;
   };
 
+  // Tiles without a mask skip the tile max: P = exp2(s*c - m_run) with the
+  // running max as it stands, and only when a lane's tile sum exceeds 256
+  // (so some P could pass E4M3's 448, or inf on the first tile) is the tile
+  // recomputed with its max (softmax_fix).  The running max never exceeds the
+  // true row max, so the largest P of a row stays >= 1, as with the max path.
+  auto to_e4m3 = [&](const float (&p)[KB][16], intx8& pf) FA_INLINE {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, r0 = 4 * (w & 3);
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r0], p[kb][r0 + 1], 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(p[kb][r0 + 2], p[kb][r0 + 3], v, true);
+      pf[w] = v;
+    }
+  };
+  auto softmax_fast = [&](const floatx16 (&s)[KB], intx8& pf, float& lsum_out) FA_INLINE -> bool {
+    float lsum = 0.0f;
+    float p[KB][16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_run));
+        lsum += p[kb][r];
+      }
+    to_e4m3(p, pf);
+    lsum_out = lsum;
+    return __ballot(!(lsum <= 256.0f)) != 0;
+  };
+  auto softmax_fix = [&](const floatx16 (&s)[KB], intx8& pf, float& lsum_out) FA_INLINE -> float {
+    float ext = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = NEG_SCALE ? fminf(ext, s[kb][r]) : fmaxf(ext, s[kb][r]);
+    ext = NEG_SCALE ? wave_min_halves(ext) : wave_max_halves(ext);
+    const float m_new = fmaxf(m_run, ext * c_log2);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.0f;
+    float p[KB][16];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, -m_new));
+        lsum += p[kb][r];
+      }
+    to_e4m3(p, pf);
+    lsum_out = lsum;
+    return alpha;
+  };
+
   // O^T += V^T P^T over the tile's 64 keys, 4 blocks of 32 head columns
   auto accumulate = [&](const char* vs, const intx8& pf) FA_INLINE {
 #pragma unroll
@@ -318,10 +370,24 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     intx8 pn;
     bool rs = false;
     float alpha = 1.0f;
-    if constexpr (HAS_S1) alpha = softmax(s1, pn, key_lim - (j + 1) * MX_BC, mask1_tag, rs);
+    constexpr bool FAST = !decltype(mask1_tag)::value;
+    float lsum_f = 0.0f;
+    bool fix = false;
+    if constexpr (HAS_S1) {
+      if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f);
+      else alpha = softmax(s1, pn, key_lim - (j + 1) * MX_BC, mask1_tag, rs);
+    }
     accumulate(vbuf(P), pb);
     if constexpr (HAS_S1) {
       asm volatile("" ::"v"(pn));
+      if constexpr (FAST) {
+        keep(lsum_f);
+        if (fix) {
+          alpha = softmax_fix(s1, pn, lsum_f);
+          rs = true;
+        }
+        l_run = l_run * alpha + lsum_f;
+      }
       keep(l_run);
       if (rs) rescale_o(alpha);
       pb = pn;
@@ -515,8 +581,9 @@ int launch_mx_quantize_vt(const void* V, void* Vt, void* Vs, int64_t BH, int64_t
 }
 
 const char* mxfp8_config_string() {
-  return "gfx950 fa_fwd_mxfp8 v1: BR=128 (4 waves x 32 rows), BC=64, 3-stage pipeline, "
-         "v_mfma_scale_f32_32x32x64_f8f6f4 for S^T=K.Q^T and O^T+=V^T.P^T, P in E4M3 (scale 1)";
+  return "gfx950 fa_fwd_mxfp8 v2: BR=128 (4 waves x 32 rows), BC=64, 3-stage pipeline, "
+         "v_mfma_scale_f32_32x32x64_f8f6f4 for S^T=K.Q^T and O^T+=V^T.P^T, P in E4M3 (scale 1), "
+         "no tile max unless a tile sum exceeds 256";
 }
 
 }  // namespace fa06
