@@ -76,7 +76,10 @@ typedef enum fa_status {
  * Execution: asynchronous on `stream`; the function never synchronises.  The
  * outputs are valid once the caller has synchronised the stream.  It
  * launches one kernel, is reentrant, and calls on different streams may run
- * concurrently.
+ * concurrently.  After one call on a device (which caches its architecture
+ * check), calls issue nothing but kernel launches -- no memset, copy or
+ * allocation -- so they can be captured in a HIP graph and replayed; the
+ * same holds for every entry point of this header.
  *
  * Errors: arguments are validated before any HIP call, shapes first, then
  * pointers (a pointer may be NULL only when its buffer holds zero bytes, as
