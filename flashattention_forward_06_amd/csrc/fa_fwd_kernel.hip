@@ -412,6 +412,50 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return alpha;
   };
 
+  // The same for unmasked tiles with a bias: the logits t = s*c + b*log2(e)
+  // are written over the scores, P = exp2(t - m_run).  A row that has seen
+  // only -inf logits so far gives NaN (-inf - -inf), which also sends the
+  // tile to the slow path (softmax_fix_logits), where such rows keep P = 0.
+  auto softmax_fast_bias = [&](floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB],
+                               float& lsum_out) FA_INLINE -> bool {
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float t = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
+        s[kb][r] = t;
+        const float p = __builtin_amdgcn_exp2f(t - m_run);
+        lsum += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    lsum_out = lsum;
+    return __ballot(!(lsum <= 65536.0f)) != 0;
+  };
+  auto softmax_fix_logits = [&](const floatx16 (&t)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> float {
+    float ext = t[0][0];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ext = fmaxf(ext, t[kb][r]);
+    const float m_new = fmaxf(m_run, wave_max_halves(ext));
+    const bool empty = m_new == -__builtin_inff();
+    const float alpha = empty ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_use = empty ? 0.0f : m_new;
+    m_run = m_new;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(t[kb][r] - m_use);
+        lsum += p;
+        pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
+      }
+    lsum_out = lsum;
+    return alpha;
+  };
+
   auto rescale_o = [&](float alpha) FA_INLINE {
 #pragma unroll
     for (int i = 0; i < NCB; ++i)
@@ -460,11 +504,13 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     bf16x8 pn[2 * KB];
     bool rs = false;
     float alpha = 1.0f;
-    constexpr bool FAST = !BIAS && !decltype(mask1_tag)::value;
+    // unmasked tiles take the fast path (no tile max), masked ones the max path
+    constexpr bool FAST = !decltype(mask1_tag)::value;
     float lsum_f = 0.0f;
     bool fix = false;
     if constexpr (HAS_S1) {
-      if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f);
+      if constexpr (FAST && BIAS) fix = softmax_fast_bias(s1, bcur, pn, lsum_f);
+      else if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f);
       else alpha = softmax(s1, bcur, pn, key_lim - (j + 1) * BC, mask1_tag, rs);
     }
     accumulate(vbuf(P), pb);
@@ -474,7 +520,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if constexpr (FAST) {
         keep(lsum_f);
         if (fix) {
-          alpha = softmax_fix(s1, pn, lsum_f);
+          if constexpr (BIAS) alpha = softmax_fix_logits(s1, pn, lsum_f);
+          else alpha = softmax_fix(s1, pn, lsum_f);
           rs = true;
         }
         l_run = l_run * alpha + lsum_f;
