@@ -115,6 +115,16 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
       if ((__int128)31 * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
     }
   }
+  // key split: the plan and its size limits
+  if (n_splits < 0 || n_splits > kSplitMax) return FA_ERR_UNSUPPORTED;
+  const SplitPlan plan = plan_split(BH, Nq, Nk, n_splits);
+  if (plan.n_splits > 1) {
+    // fp32 partial rows of one (range, head) slice use 32-bit byte offsets;
+    // the merge grid (B*H*Nq / 4 blocks at d_v = 256) stays below 2^31
+    if (Nq * dv * 4 > INT32_MAX) return FA_ERR_UNSUPPORTED;
+    if (BH * Nq > (int64_t(1) << 33) - 4) return FA_ERR_UNSUPPORTED;
+    if (BH * ((Nq + 127) / 128) * plan.n_splits > INT32_MAX) return FA_ERR_UNSUPPORTED;
+  }
   // a pointer may be NULL only when its buffer is empty
   if ((BH * Nq > 0 && (!Q || !O || !LSE)) || (BH > 0 && (!K || !V))) return FA_ERR_NULL_POINTER;
   // one workgroup per 128 query rows of a head; the grid has < 2^31 workgroups
@@ -133,16 +143,7 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
       overlaps(LSE, l_bytes, V, v_bytes) || overlaps(LSE, l_bytes, O, o_bytes) ||
       overlaps(O, o_bytes, bias, b_bytes) || overlaps(LSE, l_bytes, bias, b_bytes))
     return FA_ERR_ALIAS;
-  // key split: the plan, its limits and the caller's workspace
-  if (n_splits < 0 || n_splits > kSplitMax) return FA_ERR_UNSUPPORTED;
-  const SplitPlan plan = plan_split(BH, Nq, Nk, n_splits);
-  if (plan.n_splits > 1) {
-    // fp32 partial rows of one (range, head) slice use 32-bit byte offsets;
-    // the merge grid (rows / 4 blocks at most) and the workspace size fit
-    if (Nq * dv * 4 > INT32_MAX) return FA_ERR_UNSUPPORTED;
-    if (BH * Nq > (int64_t(1) << 35)) return FA_ERR_UNSUPPORTED;
-    if (BH * ((Nq + 127) / 128) * plan.n_splits > INT32_MAX) return FA_ERR_UNSUPPORTED;
-  }
+  // key split: the caller's workspace
   const int64_t ws_need = split_workspace_bytes(plan, BH, Nq, dv);
   if (plan.n_splits > 1) {
     if (workspace == nullptr || workspace_bytes < ws_need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;

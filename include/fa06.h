@@ -175,7 +175,7 @@ int fa_fwd_dv(const void *Q, const void *K, const void *V, void *O, float *LSE,
  *   workspace_bytes  its size.
  *   every other argument, ownership, execution and errors as for fa_fwd_dv;
  *   with more than one range, Nq * dv * 4 must stay below 2^31 and B*H*Nq
- *   at most 2^35 (else FA_ERR_UNSUPPORTED).  Two kernels are enqueued.
+ *   below 2^33 (else FA_ERR_UNSUPPORTED).  Two kernels are enqueued.
  */
 int fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *LSE,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,

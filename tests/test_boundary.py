@@ -332,6 +332,8 @@ def test_split_workspace_rules():
     assert call_split(ws=Op + 64) == 4              # overlaps O
     assert call_split(ws=Kp - 16) == 4              # overlaps K
     assert call_split(n=1025) == 3 and call_split(n=-1) == 3
+    # B*H*Nq at 2^33 rows: the merge grid at d_v = 256 would pass 2^31 blocks
+    assert call_split(B=1 << 12, H=1 << 11, Nq=1 << 10, Nk=1 << 12, d=256, dv=256, n=2, ws_bytes=1 << 62) == 3
     assert call_split(Nq=0) == 0                    # empty problem: no-op
     import torch
     if torch.cuda.is_available():
