@@ -248,6 +248,19 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
   if (B > 0 && H > INT64_MAX / B) return FA_ERR_INVALID_SHAPE;
   const int64_t BH = B * H;
   if (BH > (INT64_MAX / (dmax * 2)) / max_seq(dmax)) return FA_ERR_INVALID_SHAPE;
+  // bias: the forward's rules, plus the span of one key column over all
+  // query rows (the dK/dV kernel addresses it with 32-bit byte offsets)
+  int64_t b_bytes = 0;
+  if (bias != nullptr) {
+    if (bias_sb < 0 || bias_sh < 0 || bias_sq < 0) return FA_ERR_UNSUPPORTED;
+    if (BH * Nq > 0) {
+      const __int128 ext = (__int128)(B - 1) * bias_sb + (__int128)(H - 1) * bias_sh +
+                           (__int128)(Nq - 1) * bias_sq + Nk;
+      if (ext > kBiasMaxExtent) return FA_ERR_INVALID_SHAPE;
+      b_bytes = (int64_t)ext * 4;
+      if ((__int128)(Nq - 1) * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
+    }
+  }
   const bool has_q = BH * Nq > 0, has_k = BH > 0;
   if ((has_q && (!Q || !O || !dO || !LSE || !dQ || !D)) || (has_k && (!K || !V || !dK || !dV)))
     return FA_ERR_NULL_POINTER;
@@ -257,20 +270,8 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
   if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) || !aligned(dO, 16) ||
       !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(LSE, 4) || !aligned(D, 4))
     return FA_ERR_UNSUPPORTED;
-  // bias: the forward's rules, plus the span of one key column over all
-  // query rows (the dK/dV kernel addresses it with 32-bit byte offsets)
-  int64_t b_bytes = 0;
-  if (bias != nullptr) {
-    if (bias_sb < 0 || bias_sh < 0 || bias_sq < 0) return FA_ERR_UNSUPPORTED;
-    if (!aligned(bias, 16) || bias_sb % 4 != 0 || bias_sh % 4 != 0 || bias_sq % 4 != 0) return FA_ERR_UNSUPPORTED;
-    if (BH * Nq > 0) {
-      const __int128 ext = (__int128)(B - 1) * bias_sb + (__int128)(H - 1) * bias_sh +
-                           (__int128)(Nq - 1) * bias_sq + Nk;
-      if (ext > kBiasMaxExtent) return FA_ERR_INVALID_SHAPE;
-      b_bytes = (int64_t)ext * 4;
-      if ((__int128)(Nq - 1) * bias_sq + Nk + 128 > kBiasWaveSpan) return FA_ERR_UNSUPPORTED;
-    }
-  }
+  if (bias != nullptr && (!aligned(bias, 16) || bias_sb % 4 != 0 || bias_sh % 4 != 0 || bias_sq % 4 != 0))
+    return FA_ERR_UNSUPPORTED;
   const int64_t q_bytes = BH * Nq * d * 2, k_bytes = BH * Nk * d * 2, v_bytes = BH * Nk * dv * 2;
   const int64_t o_bytes = BH * Nq * dv * 2, l_bytes = BH * Nq * 4;
   struct Buf {
