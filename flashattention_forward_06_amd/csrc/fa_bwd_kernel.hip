@@ -239,9 +239,10 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       }
   };
 
-  // Causal kernel: one block of 64 query rows as two sub-blocks of 32, in
-  // order (the pipelined form needs more registers than a wave has once
-  // the masked steps are in the same kernel).
+  // Sequential step: one block of 64 query rows as two sub-blocks of 32, in
+  // order, for the kernels where the pipelined form below would need more
+  // registers than a wave has (a bias; the causal mask at (192, 128) and 64,
+  // where it is also no faster).
   // MASK steps hide the pairs above the causal diagonal and, with a bias,
   // the rows past Nq of a ragged last block (whose zero Q and LSE would
   // otherwise give P = exp(bias), possibly infinite).
@@ -367,7 +368,12 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
       load_bias(qb, 1, bb2[1]);
     }
     if (qb + 1 < n_qb) stage_in(qb + 1, st ^ 1);
-    if constexpr (CAUSAL || BIAS) {
+    if constexpr (CAUSAL && !BIAS && DQK == 128 && DV == 128) {
+      // causal at head size 128: the pipelined step, masked on every block
+      // (one variant in the loop fits the registers; two did not), +6 %
+      // over the sequential step
+      step(qb, st, std::true_type{});
+    } else if constexpr (CAUSAL || BIAS) {
       // Where two step variants in one loop make the compiler spill (a bias
       // without the causal mask; the causal mask at (d, d_v) = (192, 128)),
       // every step is the masked one: its masks are exact on every block,
@@ -678,8 +684,9 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 }
 
 const char* bwd_config_string() {
-  return "gfx950 fa_bwd v2: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
-         "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave; no atomics";
+  return "gfx950 fa_bwd v3: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
+         "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
+         "(causal at d=128 too); head sizes 64, 128, 192/128; fp32 bias; no atomics";
 }
 
 }  // namespace fa06
