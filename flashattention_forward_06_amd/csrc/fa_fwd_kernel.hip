@@ -35,18 +35,19 @@
 //     the exponentials overlap the matrix products of the same wave.
 //   * LDS rows are 2*d (K) and 2*d_v (V) bytes; 16-byte chunks are
 //     XOR-swizzled per row so the K fragment reads (ds_read_b128) and the V
-//     transposing reads are free of bank conflicts (the swizzled shared memory of the 5090 article's
-//     "v2", re-derived for the gfx950 LDS).
+//     transposing reads are free of bank conflicts (the swizzled shared
+//     memory of the 5090 article's "v2", re-derived for the gfx950 LDS).
 //   * The softmax scale is folded into exp2 as scale*log2(e).  The running
 //     max is only raised when it has to be; otherwise the stale max is kept,
 //     which is exact because the same max enters P, the row sum and the
 //     output.  Tiles without a mask or bias do not even compute their max:
 //     P = exp2(s*scale*log2(e) - m) uses the running max as it stands (bf16 P
 //     has fp32's exponent range), and only when a lane's tile sum exceeds
-//     2^16 (or is inf, as on the first tile) is the tile recomputed with its
-//     max.  Masked and biased tiles raise the max when the tile's exceeds it
-//     by more than RESCALE_SLACK.  This removes almost all O rescaling and
-//     most of the max reductions from the loop.
+//     2^16 (or is inf or NaN: the first tile, or a row that has only seen
+//     -inf bias) is the tile recomputed with its max.  Tiles with a bias do
+//     the same on their logits.  Masked tiles (causal diagonal, ragged end)
+//     raise the max when the tile's exceeds it by more than RESCALE_SLACK.
+//     This removes almost all O rescaling and most max reductions.
 //   * Global accesses use buffer resources sized to each (batch, head)
 //     slice: rows past Nq / Nk read as zero and stores past Nq are dropped,
 //     so ragged sequence lengths need no special load or store paths.
@@ -58,6 +59,9 @@
 //     diagonal are masked per key, and the q-tiles with the most work are
 //     dispatched first) and an fp32 additive bias with arbitrary broadcast
 //     strides, read straight from memory into registers one tile ahead.
+//   * Key split (SPLIT): workgroup (head, range, q-tile) attends to one range
+//     of keys and writes fp32 partial results; fa_fwd_merge_kernel combines
+//     the ranges (for launches with fewer than two workgroups per CU).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
