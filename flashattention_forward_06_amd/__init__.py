@@ -370,6 +370,57 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
     return dq, dk, dv, delta
 
 
+def _attention_function():
+    """torch.autograd.Function over fa_fwd / fa_bwd, built on first use (torch
+    is imported lazily, as everywhere in this module)."""
+    global _AttentionFn
+    if _AttentionFn is not None:
+        return _AttentionFn
+    import torch
+
+    class _Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, scale, causal, bias):
+            o, lse = fa_fwd(q, k, v, scale=scale, causal=causal, bias=bias)
+            ctx.save_for_backward(q, k, v, o, lse)
+            ctx.scale, ctx.causal, ctx.bias = scale, causal, bias
+            return o
+
+        @staticmethod
+        def backward(ctx, do):
+            q, k, v, o, lse = ctx.saved_tensors
+            dq, dk, dv, _ = fa_bwd(q, k, v, o, lse, do.contiguous(), scale=ctx.scale, causal=ctx.causal,
+                                   bias=ctx.bias)
+            return dq, dk, dv, None, None, None
+
+    _AttentionFn = _Attention
+    return _AttentionFn
+
+
+_AttentionFn = None
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = False, bias=None):
+    """Differentiable attention for training: O = softmax(scale Q K^T + bias) V.
+
+    The forward pass is ``fa_fwd`` and the backward pass ``fa_bwd`` (gradients
+    by recomputation from the forward's log-sum-exp), both in this library's
+    HIP kernels; O and the log-sum-exp are kept for the backward pass.
+    q, k: bf16 [B, H, N, d], v: bf16 [B, H, Nk, dv] on one HIP device, (d, dv)
+    one of (64, 64), (128, 128), (192, 128) when gradients are needed
+    ((256, 256) runs forward only).  ``scale`` defaults to 1/sqrt(d).  No
+    gradient flows to ``bias``: pass a bias that does not require one.
+    Returns O, bf16 [B, H, Nq, dv].
+    """
+    import torch
+
+    if bias is not None and isinstance(bias, torch.Tensor) and bias.requires_grad:
+        raise NotImplementedError("attention(): no gradient is formed for the bias; pass bias.detach()")
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _attention_function().apply(q, k, v, float(scale), bool(causal), bias)
+
+
 def fa_mxfp8_build_info() -> str:
     return load_library().fa_mxfp8_build_info().decode()
 
@@ -456,5 +507,5 @@ def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, c
     return out, lse
 
 
-__all__ = ["fa_bwd_dv_raw", "fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
+__all__ = ["attention", "fa_bwd_dv_raw", "fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
            "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes"]

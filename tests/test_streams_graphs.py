@@ -1,6 +1,8 @@
 """Execution contract of the C ABI on the GPU: calls on different streams run
-concurrently and give the same bits as sequential calls, and the launches
-can be captured in a HIP graph (through torch.cuda.graph) and replayed.
+concurrently and give the same bits as sequential calls, the launches can be
+captured in a HIP graph (through torch.cuda.graph) and replayed, and the
+autograd entry point (attention) gives exactly fa_fwd's output and fa_bwd's
+gradients.
 
 Every kernel here is deterministic (no atomics), so results are compared
 bit for bit.  Graph tests replay several times with eager work and new
@@ -129,3 +131,26 @@ def test_backward_graph_replays(fa):
         torch.cuda.synchronize()
         for a, b in zip(got, want):
             assert same(a, b), f"backward replay {rep} differs from the eager call"
+
+
+@pytest.mark.parametrize("d,dv,causal,with_bias", [(128, 128, False, False), (128, 128, True, True),
+                                                   (192, 128, True, False), (64, 64, False, True)])
+def test_autograd_attention_matches_direct_calls(fa, d, dv, causal, with_bias):
+    import torch
+    say(f"case autograd attention d={d} d_v={dv} causal={causal} bias={with_bias}")
+    Q, K, V = fi.make_qkv(2, 2, 200, 333, d, seed=630, dv=dv)
+    q, k, v = (to_dev(x).requires_grad_(True) for x in (Q, K, V))
+    bias = torch.randn((1, 2, 1, 333), device="cuda") if with_bias else None
+    o = fa.attention(q, k, v, causal=causal, bias=bias)
+    # a non-contiguous upstream gradient (a transposed view)
+    g = torch.randn((2, 2, dv, 200), device="cuda").to(torch.bfloat16).transpose(2, 3)
+    o.backward(g)
+    torch.cuda.synchronize()
+    qd, kd, vd = (x.detach() for x in (q, k, v))
+    o2, lse2 = fa.fa_fwd(qd, kd, vd, causal=causal, bias=bias)
+    dq, dk, dv_, _ = fa.fa_bwd(qd, kd, vd, o2, lse2, g.contiguous(), causal=causal, bias=bias)
+    torch.cuda.synchronize()
+    assert same(o.detach(), o2)
+    assert same(q.grad, dq) and same(k.grad, dk) and same(v.grad, dv_)
+    with pytest.raises(NotImplementedError):
+        fa.attention(qd, kd, vd, bias=torch.zeros((1, 2, 1, 333), device="cuda", requires_grad=True))
