@@ -6,8 +6,10 @@ The library is built in-tree next to this file.
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -22,17 +24,33 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
-    out = out or LIB_PATH
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *HIP_FLAGS, *(extra_flags or []), "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError(f"hipcc failed with status {r.returncode}")
+        raise RuntimeError(f"hipcc failed with status {r.returncode}: {' '.join(cmd[-3:])}")
+
+
+def build(verbose: bool = False, extra_flags=None, out: str | None = None) -> str:
+    """Compile every source to an object in parallel (one hipcc per source),
+    then link the shared library; the result replaces ``out`` atomically."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    out = out or LIB_PATH
+    tmp = out + ".tmp"
+    objdir = tempfile.mkdtemp(prefix="fa06_build_")
+    try:
+        objs = [os.path.join(objdir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        cmds = [[HIPCC, *HIP_FLAGS, *(extra_flags or []), f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+                 os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(cmds), os.cpu_count() or 1)) as pool:
+            for f in [pool.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        _run([HIPCC, *HIP_FLAGS, *(extra_flags or []), "-shared", *objs, "-o", tmp], verbose)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     os.replace(tmp, out)
     return out
 
