@@ -113,12 +113,10 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   const int c = lane & 31;
   const int h = lane >> 5;
 
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  const int nfull = nblk & ~7;
-  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
-  const int bh = bid / n_ktiles;
-  const int kt = bid - bh * n_ktiles;
+  // causal: key tile 0 is seen by the most query rows, so ascending tiles
+  // are longest-first
+  int bh, kt;
+  xcd_tile_map(blockIdx.x, gridDim.x, n_ktiles, CAUSAL, bh, kt);
   const int k0 = kt * KV_KEYS;
   const int kw = k0 + wave * 32;  // this wave's first key
   const int key = kw + c;         // this lane's key
@@ -422,13 +420,9 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int c = lane & 31;
   const int h = lane >> 5;
 
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  const int nfull = nblk & ~7;
-  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
-  const int bh = bid / n_qtiles;
-  int qt = bid - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
+  int bh, qt;
+  xcd_tile_map(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows start first
   const int q0 = qt * DQ_ROWS;
   const int q = q0 + wave * 32 + c;  // this lane's query row
 

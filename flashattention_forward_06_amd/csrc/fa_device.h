@@ -116,6 +116,28 @@ __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char
   }
 }
 
+// Workgroup id -> (head, tile) of a grid of n_tiles tiles per head.
+// Workgroups are dispatched round-robin over the 8 XCDs, so the id is
+// remapped to give each XCD a contiguous share of the tiles (the tiles of one
+// head share that head's K/V in the XCD's L2).  With `lpt` (the tiles' work
+// falls with the tile index, as in causal attention) and a share that holds
+// whole heads, the share is ordered tile-major across its heads, so the
+// longest tiles of all those heads start first.
+__device__ inline void xcd_tile_map(int bid, int nblk, int n_tiles, bool lpt, int& bh, int& t) {
+  const int nfull = nblk & ~7;
+  const int per = nfull >> 3;
+  if (lpt && bid < nfull && per % n_tiles == 0) {
+    const int hpc = per / n_tiles;  // heads per XCD
+    const int i = bid >> 3;
+    bh = (bid & 7) * hpc + i % hpc;
+    t = i / hpc;
+    return;
+  }
+  if (bid < nfull) bid = (bid & 7) * per + (bid >> 3);
+  bh = bid / n_tiles;
+  t = bid - bh * n_tiles;
+}
+
 // Every helper lambda of a kernel is inlined: loop bodies must stay one
 // straight-line region with all state in registers.
 #define FA_INLINE __attribute__((always_inline))

@@ -125,20 +125,26 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int h = lane >> 5;   // half of the wave
 
   // XCD-aware remap: consecutive logical tiles (same head) go to one XCD.
-  int bid = blockIdx.x;
   const int nblk = gridDim.x;
-  const int nfull = nblk & ~7;
-  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
   int bh, qt, split = 0;
   if constexpr (SPLIT) {
     // logical order (head, split, q-tile): the q-tiles of one key range of
     // one head are consecutive, so they share that range in one XCD's L2
+    int bid = blockIdx.x;
+    const int nfull = nblk & ~7;
+    if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
     const int per_bh = n_splits * n_qtiles;
     bh = bid / per_bh;
     const int rem = bid - bh * per_bh;
     split = rem / n_qtiles;
     qt = rem - split * n_qtiles;
+  } else if constexpr (CAUSAL) {
+    xcd_tile_map(blockIdx.x, nblk, n_qtiles, true, bh, qt);
   } else {
+    // consecutive logical tiles (same head) go to one XCD
+    int bid = blockIdx.x;
+    const int nfull = nblk & ~7;
+    if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
     bh = bid / n_qtiles;
     qt = bid - bh * n_qtiles;
   }
