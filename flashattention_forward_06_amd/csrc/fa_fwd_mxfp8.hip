@@ -87,13 +87,18 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int c = lane & 31;
   const int h = lane >> 5;
 
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  const int nfull = nblk & ~7;
-  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
-  const int bh = bid / n_qtiles;
-  int qt = bid - bh * n_qtiles;
-  if (CAUSAL) qt = n_qtiles - 1 - qt;
+  int bh, qt;
+  if constexpr (CAUSAL) {
+    xcd_tile_map(blockIdx.x, gridDim.x, n_qtiles, true, bh, qt);  // longest-first over each XCD
+    qt = n_qtiles - 1 - qt;
+  } else {
+    int bid = blockIdx.x;
+    const int nblk = gridDim.x;
+    const int nfull = nblk & ~7;
+    if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+    bh = bid / n_qtiles;
+    qt = bid - bh * n_qtiles;
+  }
   const int q0 = qt * MX_BR;
 
   const size_t bq = (size_t)bh * (size_t)Nq, bk = (size_t)bh * (size_t)Nk;
