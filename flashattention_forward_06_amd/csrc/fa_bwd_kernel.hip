@@ -116,7 +116,13 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   // causal: key tile 0 is seen by the most query rows, so ascending tiles
   // are longest-first
   int bh, kt;
-  xcd_tile_map(blockIdx.x, gridDim.x, n_ktiles, CAUSAL, bh, kt);
+  if constexpr (BIAS) {
+    // heads that share dense bias columns run side by side (one bias fetch)
+    const HeadGroup hg = bias_head_group(gridDim.x / (n_ktiles * H), H, bias_sb, bias_sh, bias_sq);
+    grouped_tile_map(blockIdx.x, gridDim.x, n_ktiles, CAUSAL, hg, bh, kt);
+  } else {
+    xcd_tile_map(blockIdx.x, gridDim.x, n_ktiles, CAUSAL, bh, kt);
+  }
   const int k0 = kt * KV_KEYS;
   const int kw = k0 + wave * 32;  // this wave's first key
   const int key = kw + c;         // this lane's key
@@ -421,7 +427,13 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int h = lane >> 5;
 
   int bh, qt;
-  xcd_tile_map(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  if constexpr (BIAS) {
+    // heads that share dense bias rows run side by side (one bias fetch)
+    const HeadGroup hg = bias_head_group(gridDim.x / (n_qtiles * H), H, bias_sb, bias_sh, bias_sq);
+    grouped_tile_map(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, hg, bh, qt);
+  } else {
+    xcd_tile_map(blockIdx.x, gridDim.x, n_qtiles, CAUSAL, bh, qt);
+  }
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows start first
   const int q0 = qt * DQ_ROWS;
   const int q = q0 + wave * 32 + c;  // this lane's query row

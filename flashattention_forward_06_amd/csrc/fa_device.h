@@ -138,6 +138,44 @@ __device__ inline void xcd_tile_map(int bid, int nblk, int n_tiles, bool lpt, in
   t = bid - bh * n_tiles;
 }
 
+// Heads that read the same rows of a dense bias.  A bias broadcast over the
+// batch (batch stride 0), over the heads (head stride 0) or over both is one
+// block of rows for g heads at once; bh = outer * os + m * ms for member
+// m < g of group `outer`.  g = 1 when nothing is shared or the bias has no
+// rows (a per-key bias is a few KiB and stays in cache anyway).
+struct HeadGroup {
+  int g, os, ms;
+};
+__device__ inline HeadGroup bias_head_group(int B, int H, int64_t sb, int64_t sh, int64_t sq) {
+  const bool over_b = sb == 0 && B > 1;
+  const bool over_h = sh == 0 && H > 1;
+  if (sq == 0 || (!over_b && !over_h)) return {1, 1, 0};
+  if (over_b && over_h) return {B * H, 0, 1};
+  if (over_b) return {B, 1, H};  // members are the batches of head `outer`
+  return {H, H, 1};              // members are the heads of batch `outer`
+}
+
+// xcd_tile_map over "logical heads" in which the members of a bias group
+// are adjacent, and without `lpt` also innermost: workgroups that read the
+// same bias block get consecutive ids within one XCD's share, so they run
+// at the same time and the block is fetched from HBM once instead of g times.
+__device__ inline void grouped_tile_map(int bid, int nblk, int n_tiles, bool lpt, HeadGroup hg, int& bh, int& t) {
+  if (lpt) {
+    int lh;
+    xcd_tile_map(bid, nblk, n_tiles, true, lh, t);
+    const int outer = lh / hg.g;
+    bh = outer * hg.os + (lh - outer * hg.g) * hg.ms;
+    return;
+  }
+  const int nfull = nblk & ~7;
+  if (bid < nfull) bid = (bid & 7) * (nfull >> 3) + (bid >> 3);
+  const int rest = bid / hg.g;  // logical order (outer, tile, member)
+  const int m = bid - rest * hg.g;
+  const int outer = rest / n_tiles;
+  t = rest - outer * n_tiles;
+  bh = outer * hg.os + m * hg.ms;
+}
+
 // Every helper lambda of a kernel is inlined: loop bodies must stay one
 // straight-line region with all state in registers.
 #define FA_INLINE __attribute__((always_inline))

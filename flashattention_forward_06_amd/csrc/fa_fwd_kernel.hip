@@ -138,6 +138,10 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int rem = bid - bh * per_bh;
     split = rem / n_qtiles;
     qt = rem - split * n_qtiles;
+  } else if constexpr (BIAS) {
+    // heads that share dense bias rows run side by side (one bias fetch)
+    const HeadGroup hg = bias_head_group(nblk / (n_qtiles * H), H, bias_sb, bias_sh, bias_sq);
+    grouped_tile_map(blockIdx.x, nblk, n_qtiles, CAUSAL, hg, bh, qt);
   } else if constexpr (CAUSAL) {
     xcd_tile_map(blockIdx.x, nblk, n_qtiles, true, bh, qt);
   } else {

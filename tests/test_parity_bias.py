@@ -50,6 +50,10 @@ def make_bias(kind, B, H, Nq, Nk, seed):
         return (2.0 * rng.standard_normal((Nq, Nk))).astype(np.float32)
     if kind == "alibi":
         return alibi(H, Nq, Nk)
+    if kind == "batch_shared":
+        return (2.0 * rng.standard_normal((1, H, Nq, Nk))).astype(np.float32)
+    if kind == "head_shared":
+        return (2.0 * rng.standard_normal((B, 1, Nq, Nk))).astype(np.float32)
     raise ValueError(kind)
 
 
@@ -78,6 +82,13 @@ BIAS_CASES = [
     (1, 2, 64, 1, "full", False, 95, "single key"),
     (1, 2, 640, 640, "alibi", False, 96, "ALiBi-like slopes, several q tiles"),
     (1, 1, 300, 130, "full", True, 97, "causal with Nq > Nk: leading rows see no key"),
+    # bias rows shared by several heads: their workgroups are grouped in the grid
+    (3, 2, 300, 333, "batch_shared", False, 102, "[1,H,Nq,Nk] over 3 batches, ragged"),
+    (3, 2, 300, 333, "batch_shared", True, 103, "[1,H,Nq,Nk] over 3 batches, causal"),
+    (2, 3, 200, 260, "head_shared", False, 104, "[B,1,Nq,Nk] over 3 heads"),
+    (2, 3, 200, 260, "head_shared", True, 105, "[B,1,Nq,Nk] over 3 heads, causal"),
+    (2, 3, 257, 190, "rows_keys", False, 106, "[Nq,Nk] over 2 batches and 3 heads"),
+    (4, 4, 512, 256, "batch_shared", True, 107, "[1,H,Nq,Nk], whole heads per XCD share (64 workgroups)"),
 ]
 
 

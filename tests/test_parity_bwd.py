@@ -196,6 +196,10 @@ def make_bias(kind, B, H, Nq, Nk, seed):
         j = np.arange(Nk)[None, :]
         slopes = 2.0 ** -(np.arange(H) + 1.0)
         return (-slopes[:, None, None] * np.abs(i - j))[None].astype(np.float32)
+    if kind == "batch_shared":
+        return (2.0 * rng.standard_normal((1, H, Nq, Nk))).astype(np.float32)
+    if kind == "head_shared":
+        return (2.0 * rng.standard_normal((B, 1, Nq, Nk))).astype(np.float32)
     raise ValueError(kind)
 
 
@@ -207,6 +211,11 @@ BIAS_CASES = [
     (1, 2, 200, 130, False, "per_key_large", 323, "per-key bias with +60 entries, ragged last query block"),
     (1, 2, 300, 130, True, "per_key_large", 324, "per-key bias, causal with Nq > Nk"),
     (1, 4, 640, 640, True, "alibi", 325, "ALiBi-like slopes, causal, several blocks"),
+    # bias shared by several heads: their workgroups are grouped in the grid
+    (3, 2, 300, 333, False, "batch_shared", 326, "[1,H,Nq,Nk] over 3 batches, ragged"),
+    (3, 2, 300, 333, True, "batch_shared", 327, "[1,H,Nq,Nk] over 3 batches, causal"),
+    (2, 3, 200, 260, True, "head_shared", 328, "[B,1,Nq,Nk] over 3 heads, causal"),
+    (4, 4, 512, 512, True, "alibi", 329, "ALiBi over 4 batches, causal, whole heads per XCD share"),
 ]
 
 
