@@ -41,12 +41,13 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # Reported only while the library's build string is the one measured; any
 # other kernel build reports null.
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v5: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+    "kernel": "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
               "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on "
-              "mfma_f32_32x32x16_bf16, V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; "
-              "causal tile skipping; fp32 additive bias; key split with LSE merge",
+              "mfma_f32_32x32x16_bf16 (K fragments read two k steps ahead at head size 128), V^T via "
+              "ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; fp32 additive "
+              "bias; key split with LSE merge",
     "workload": "b2_h16_n8192",
-    "bytes": 325.0e6,
+    "bytes": 340.4e6,
 }
 
 

@@ -267,16 +267,42 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float l_run = 0.0f;               // partial row sum of this lane's keys
 
   // S^T = K Q^T for the BC keys of one K buffer (32-key blocks).
+  // The K fragments of k step t + KPF are read before the MFMAs of step t
+  // (a ring of KPF + 1 fragment sets): written in this order, the
+  // scheduler keeps the LDS reads further ahead of their use than it does
+  // for a read-then-multiply loop (1.3-1.5 % at head size 128, identical
+  // results).  The other head sizes keep KPF = 0 (read, then multiply):
+  // there the ring costs registers they do not have.
+  constexpr int KPF = DQK == 128 && DV == 128 ? 2 : 0;
   auto scores = [&](const char* ks, floatx16 (&s)[KB]) FA_INLINE {
+    auto kfrag = [&](int kb, int t) FA_INLINE {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>(kb * 32 + c, 2 * t + h)));
+    };
+    if constexpr (KPF == 0) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = floatx16{};
-      const uint32_t row = kb * 32 + c;
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = floatx16{};
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qb[t], s[kb], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kb, t), qb[t], s[kb], 0, 0, 0);
       }
+      return;
+    }
+    bf16x8 fr[KPF + 1][KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = floatx16{};
+#pragma unroll
+    for (int t = 0; t < KPF; ++t)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) fr[t][kb] = kfrag(kb, t);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (t + KPF < NT) {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) fr[(t + KPF) % (KPF + 1)][kb] = kfrag(kb, t + KPF);
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % (KPF + 1)][kb], qb[t], s[kb], 0, 0, 0);
     }
   };
 
@@ -751,8 +777,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v5: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
-         "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16, "
+  return "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+         "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
+         "(K fragments read two k steps ahead at head size 128), "
          "V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; "
          "fp32 additive bias; key split with LSE merge";
 }
