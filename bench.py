@@ -282,6 +282,15 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
+    # per-call durations, after the timed region: one event pair around each call
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in pairs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+
     ms_per_step = wall * 1e3 / args.steps
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (ev_ms * 1e-3) / 1e12
@@ -297,6 +306,8 @@ def main():
                         and not args.mxfp8 and bias is None and args.splitkv is None
                         and w.name == MEASURED_TRAFFIC["workload"]) else None),
         "kernel_ms": round(ev_ms, 4),
+        "per_call_ms": {"median": round(float(np.median(per_call)), 4), "min": round(per_call[0], 4),
+                        "max": round(per_call[-1], 4), "calls": len(per_call)},
     }
     out = {
         "metric": ("bwd" if args.bwd else "fwd") + " attention TFLOP/s (bf16, d=128, non-causal) and % of MI355X MFMA peak",
@@ -322,6 +333,10 @@ def main():
                               fa.fa_mxfp8_build_info() if args.mxfp8 else fa.fa_build_info())},
         "roofline": roof,
         "cpu_baseline": None,
+        "env": {"device": torch.cuda.get_device_name(dev),
+                "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+                "cus": torch.cuda.get_device_properties(dev).multi_processor_count,
+                "torch": torch.__version__, "hip": torch.version.hip},
     }
     if bias is not None:
         out["bias_bytes"] = bias.numel() * 4
