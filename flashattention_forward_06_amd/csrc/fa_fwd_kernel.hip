@@ -285,24 +285,24 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
         for (int t = 0; t < NT; ++t) s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag(kb, t), qb[t], s[kb], 0, 0, 0);
       }
-      return;
-    }
-    bf16x8 fr[KPF + 1][KB];
+    } else {
+      bf16x8 fr[KPF + 1][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = floatx16{};
+      for (int kb = 0; kb < KB; ++kb) s[kb] = floatx16{};
 #pragma unroll
-    for (int t = 0; t < KPF; ++t)
+      for (int t = 0; t < KPF; ++t)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) fr[t][kb] = kfrag(kb, t);
+        for (int kb = 0; kb < KB; ++kb) fr[t][kb] = kfrag(kb, t);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      if (t + KPF < NT) {
+      for (int t = 0; t < NT; ++t) {
+        if (t + KPF < NT) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) fr[(t + KPF) % (KPF + 1)][kb] = kfrag(kb, t + KPF);
+          for (int kb = 0; kb < KB; ++kb) fr[(t + KPF) % (KPF + 1)][kb] = kfrag(kb, t + KPF);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % (KPF + 1)][kb], qb[t], s[kb], 0, 0, 0);
       }
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % (KPF + 1)][kb], qb[t], s[kb], 0, 0, 0);
     }
   };
 
