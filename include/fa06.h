@@ -1,7 +1,8 @@
 /*
  * fa06.h -- C ABI of the MI355X (gfx950) fused attention forward pass.
  *
- * One operation: exact, dense, non-causal scaled-dot-product attention,
+ * The headline operation, fa_fwd: exact, dense, non-causal scaled-dot-product
+ * attention,
  *
  *     O = softmax_row(scale * Q K^T) V,    LSE_i = ln sum_j exp(scale * q_i . k_j)
  *
@@ -18,6 +19,12 @@
  * of that same section, row-major and contiguous:
  *     Q [B, H, Nq, d]   K [B, H, Nk, d]   V [B, H, Nk, d]   O [B, H, Nq, d]
  *     LSE [B, H, Nq]
+ *
+ * Around it, each with its own comment below: the mask/bias term
+ * (fa_fwd_masked), a value head size apart from the query/key one
+ * (fa_fwd_dv), a key split with a log-sum-exp merge for launches with few
+ * query tiles (fa_fwd_splitkv), the backward pass by recomputation (fa_bwd,
+ * fa_bwd_masked, fa_bwd_dv) and MXFP8 inputs (fa_fwd_mxfp8 and its encoders).
  *
  * No symbol here takes or returns a framework type; every buffer is a plain
  * device pointer.
@@ -36,7 +43,7 @@ typedef enum fa_status {
     FA_OK = 0,
     FA_ERR_NULL_POINTER = 1,  /* a pointer to a non-empty buffer is NULL          */
     FA_ERR_INVALID_SHAPE = 2, /* B, H or Nq negative, Nk < 1, or sizes overflow    */
-    FA_ERR_UNSUPPORTED = 3,   /* d != 128, misaligned pointer, or N above FA_MAX_SEQ */
+    FA_ERR_UNSUPPORTED = 3,   /* head size not built, misaligned pointer, N too large */
     FA_ERR_ALIAS = 4,         /* O or LSE overlaps Q, K, V or each other           */
     FA_ERR_INVALID_SCALE = 5, /* scale is NaN or infinite                          */
     FA_ERR_DEVICE = 6,        /* no HIP device, or the current device is not gfx950 */
