@@ -91,19 +91,19 @@ constexpr int kv_lds(int dqk, int dv) { return 2 * KV_QB * 2 * (dqk + dv) + 4 * 
 // Largest finite float: the clamp of -LSE * log2(e) for rows that saw no key.
 constexpr float NL_MAX = 3.0e38f;
 
-// Waves per SIMD of the dK/dV and dQ kernels.  At head size 64 without a
-// bias both kernels fit two waves' registers (<= 256 each, no spills) and
-// their LDS (33 KiB / 32 KiB per workgroup) allows two workgroups per CU:
-// the second wave hides the first's latency (backward at head size 64:
-// +46 %, causal +38 %, identical results).  Everything else needs more than
-// 256 registers (accumulators, K/V or Q/dO operands and the S/dP tiles) and
-// runs one wave per SIMD, so the interleave of each wave's own MFMA and VALU
-// work is all the overlap there is.
-constexpr int bwd_waves_per_simd(int dqk, bool bias) { return dqk == 64 && !bias ? 2 : 1; }
+// Waves per SIMD of the dK/dV and dQ kernels.  At head size 64 both kernels
+// fit two waves' registers (<= 256 each; without a bias no spills, with one
+// 18-33 spilled registers) and their LDS (33 KiB / 32 KiB per workgroup)
+// allows two workgroups per CU: the second wave hides the first's latency
+// (backward at head size 64: +46 %, causal +38 %, with a bias +20 %, identical
+// results).  Larger head sizes need more than 256 registers (accumulators,
+// K/V or Q/dO operands and the S/dP tiles) and run one wave per SIMD, so the
+// interleave of each wave's own MFMA and VALU work is all the overlap there is.
+constexpr int bwd_waves_per_simd(int dqk) { return dqk == 64 ? 2 : 1; }
 
 template <int DQK, int DV, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK, BIAS), bwd_waves_per_simd(DQK, BIAS))))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK), bwd_waves_per_simd(DQK))))
 fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ Dl,
@@ -417,7 +417,7 @@ constexpr int dq_lds(int dqk, int dv) { return 2 * DQ_BC * 2 * (dqk + dv); }
 
 template <int DQK, int DV, bool CAUSAL, bool BIAS>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK, BIAS), bwd_waves_per_simd(DQK, BIAS))))
+__attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK), bwd_waves_per_simd(DQK))))
 fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                  const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
                  const float* __restrict__ LSE, const float* __restrict__ Dl, uint16_t* __restrict__ dQ,
@@ -702,7 +702,7 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 const char* bwd_config_string() {
   return "gfx950 fa_bwd v4: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
-         "(causal at d=128 too); two waves per SIMD at head size 64 without bias; head sizes 64, 128, 192/128; "
+         "(causal at d=128 too); two waves per SIMD at head size 64; head sizes 64, 128, 192/128; "
          "fp32 bias; no atomics";
 }
 
