@@ -244,8 +244,8 @@ def main():
                      o.data_ptr(), lse.data_ptr(), w.B, w.H, w.Nq, w.Nk, w.d, vt8.shape[3],
                      ctypes.c_float(w.scale), int(args.causal), sptr)
     if args.bwd:
-        if (w.d, w.d_v) not in ((64, 64), (128, 128), (192, 128)) or args.splitkv is not None:
-            raise SystemExit("--bwd takes (d, d_v) = (64, 64), (128, 128) or (192, 128) and no --splitkv")
+        if (w.d, w.d_v) not in ((64, 64), (128, 128), (256, 256), (192, 128)) or args.splitkv is not None:
+            raise SystemExit("--bwd takes (d, d_v) = (64, 64), (128, 128), (256, 256) or (192, 128) and no --splitkv")
         dO = fi.make_qkv(w.B, w.H, w.Nq, 1, w.d_v, seed=w.seed + 5000)[0]
         g = up(dO)
         rc = call(*call_args)  # forward once: O and LSE

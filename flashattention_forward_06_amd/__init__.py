@@ -308,7 +308,7 @@ def fa_bwd(q, k, v, o, lse, do, scale: float | None = None, causal: bool = False
     """Attention backward on torch tensors: gradients of a loss through O.
 
     q, k: bf16 [B, H, N, d], v, o, do: [B, H, N, dv], contiguous on one HIP
-    device, (d, dv) one of (64, 64), (128, 128), (192, 128) (o and
+    device, (d, dv) one of (64, 64), (128, 128), (256, 256), (192, 128) (o and
     lse are the outputs of ``fa_fwd`` for the same q, k, v, scale, causal
     flag and bias; lse fp32 [B, H, Nq]).  ``bias``: the forward's fp32 bias
     (broadcastable to [B, H, Nq, Nk]); no gradient is formed for it.
@@ -407,8 +407,8 @@ def attention(q, k, v, scale: float | None = None, causal: bool = False, bias=No
     by recomputation from the forward's log-sum-exp), both in this library's
     HIP kernels; O and the log-sum-exp are kept for the backward pass.
     q, k: bf16 [B, H, N, d], v: bf16 [B, H, Nk, dv] on one HIP device, (d, dv)
-    one of (64, 64), (128, 128), (192, 128) when gradients are needed
-    ((256, 256) runs forward only).  ``scale`` defaults to 1/sqrt(d).  No
+    one of (64, 64), (128, 128), (256, 256), (192, 128).  ``scale``
+    defaults to 1/sqrt(d).  No
     gradient flows to ``bias``: pass a bias that does not require one.
     Returns O, bf16 [B, H, Nq, dv].
     """

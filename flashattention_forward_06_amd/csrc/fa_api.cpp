@@ -230,10 +230,12 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
 
 namespace {
 
-// (d, dv) pairs with backward kernels: the dK/dV kernel keeps K and V rows
-// and both accumulators in registers, which head size 256 exceeds.
+// (d, dv) pairs with backward kernels.  At head size 256 the kernels keep
+// more in registers than one wave holds (K and V rows and both accumulators
+// in the dK/dV kernel): they run, with spills to scratch memory, and without
+// a bias.
 bool bwd_head_sizes_supported(int64_t d, int64_t dv) {
-  return (d == dv && (d == 64 || d == 128)) || (d == 192 && dv == 128);
+  return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
 
 int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -242,6 +244,7 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
                             const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (!bwd_head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
+  if (d == 256 && bias != nullptr) return FA_ERR_UNSUPPORTED;  // no bias kernels at head size 256
   const int64_t dmax = d > dv ? d : dv;
   if (Nq > max_seq(dmax) || Nk > max_seq(dmax)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
@@ -448,7 +451,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a pointer to a non-empty buffer is NULL";
     case FA_ERR_INVALID_SHAPE: return "FA_ERR_INVALID_SHAPE: B, H, Nq must be >= 0, Nk >= 1, and sizes must fit";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: d must be 64, 128 or 256 (128 for fa_bwd), N <= min(2^23, 2^30/d), "
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: (d, d_v) must be (64, 64), (128, 128), (256, 256) or (192, 128) "
+                                     "(d = 128 for MXFP8), N <= min(2^23, 2^30/d), "
                                      "pointers 16-byte aligned (LSE 4), "
                                      "bias strides non-negative multiples of 4 within the addressable span";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: O or LSE overlaps Q, K, V or each other";

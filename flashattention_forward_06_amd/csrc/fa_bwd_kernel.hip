@@ -566,6 +566,12 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // one tile ahead so its latency hides behind a tile of work; at (192, 128)
   // the registers for that are not there, and each tile loads its own)
   constexpr bool BIAS_AHEAD = DQK + DV <= 256;
+  // Explicit MFMA/VALU interleave of each step.  Not at head size 256: that
+  // build spills ~100 registers to scratch, and with the interleave groups
+  // its dQ came out wrong on the masked tiles (causal diagonal, ragged last
+  // tile) while the unmasked tiles and every other head size were right; the
+  // default schedule of the same source matches the oracle there.
+  constexpr bool DQ_INTERLEAVE = DQK != 256;
   floatx4 bt[2][4], bn[2][4];
   if constexpr (BIAS && BIAS_AHEAD) {
     if (n_tiles > 0) load_bias(0, bt);
@@ -585,17 +591,21 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     sdp(ks, vs, 1, s1, dp1);
     dsoft(s0, dp0, 0, lim, mask_tag, bt[0], ds0);
     // the MFMAs of S/dP(1), each followed by 5 VALU of the softmax of block 0
+    if constexpr (DQ_INTERLEAVE) {
 #pragma unroll
-    for (int i = 0; i < NTQ + NTV; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      for (int i = 0; i < NTQ + NTV; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
     }
     dq_acc(ks, 0, ds0);
     dsoft(s1, dp1, 1, lim, mask_tag, bt[1], ds1);
+    if constexpr (DQ_INTERLEAVE) {
 #pragma unroll
-    for (int i = 0; i < 2 * NCQ; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      for (int i = 0; i < 2 * NCQ; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      }
     }
     dq_acc(ks, 1, ds1);
     if constexpr (BIAS && BIAS_AHEAD) {
@@ -636,13 +646,21 @@ BwdKernels bwd_kernels() {
   k.delta = (const void*)&fa_bwd_delta_kernel<DV>;
   k.delta_rows_per_block = 256 / (DV / 8);
   k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false>;
-  k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true>;
   k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false>;
-  k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true>;
   k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false>;
-  k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true>;
   k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false>;
-  k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true>;
+  // Head size 256 has no bias variant: built with a bias, its dQ kernel
+  // (about 150 registers spilled to scratch) returned non-finite dQ on every
+  // bias layout tested while its dK/dV were right; the entry points reject a
+  // bias at that size instead.
+  if constexpr (DQK == 256) {
+    k.dkdv[0][1] = k.dkdv[1][1] = k.dq[0][1] = k.dq[1][1] = nullptr;
+  } else {
+    k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true>;
+    k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true>;
+    k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true>;
+    k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true>;
+  }
   return k;
 }
 
@@ -653,6 +671,7 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.d == 64 && a.dv == 64) kn = bwd_kernels<64, 64>();
   else if (a.d == 128 && a.dv == 128) kn = bwd_kernels<128, 128>();
   else if (a.d == 192 && a.dv == 128) kn = bwd_kernels<192, 128>();
+  else if (a.d == 256 && a.dv == 256) kn = bwd_kernels<256, 256>();
   else return 1;
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
@@ -680,6 +699,7 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   int heads = (int)a.H;
   const int ci = a.causal ? 1 : 0;
   const int bi = bias != nullptr ? 1 : 0;
+  if (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr) return 1;
   {
     int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
@@ -702,7 +722,7 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 const char* bwd_config_string() {
   return "gfx950 fa_bwd v4: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
-         "(causal at d=128 too); two waves per SIMD at head size 64; head sizes 64, 128, 192/128; "
+         "(causal at d=128 too); two waves per SIMD at head size 64; head sizes 64, 128, 192/128, 256 (spills); "
          "fp32 bias; no atomics";
 }
 

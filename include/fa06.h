@@ -222,9 +222,13 @@ int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t
  *   D        device, fp32 [B, H, Nq] workspace owned by the caller; receives
  *            D_i = dO_i . O_i.
  *   B, H, Nq, Nk, scale, causal, stream  as for fa_fwd_masked (no bias).
- *   d        64 or 128 (FA_HEAD_DIM); other values return FA_ERR_UNSUPPORTED
- *            (256 included: the dK/dV kernel keeps K, V and both
- *            accumulators in registers, which that size exceeds).
+ *   d        64, 128 (FA_HEAD_DIM) or 256; other values return
+ *            FA_ERR_UNSUPPORTED.  At 256 the kernels need more registers
+ *            than one wave holds (the dK/dV kernel keeps K, V and both
+ *            accumulators in registers) and spill to scratch memory: correct,
+ *            but far slower per FLOP than the smaller head sizes; with a
+ *            bias (fa_bwd_masked, fa_bwd_dv) that size returns
+ *            FA_ERR_UNSUPPORTED.
  *
  * Requirements and errors as for fa_fwd; every pointer must be 16-byte
  * aligned except LSE and D (4 bytes); an output (dQ, dK, dV, D) that overlaps
@@ -265,8 +269,8 @@ int fa_bwd_masked(const void *Q, const void *K, const void *V, const void *O, co
 /*
  * fa_bwd_dv -- fa_bwd_masked for a forward pass with value head size d_v
  * apart from the query/key head size d (fa_fwd_dv's shapes): Q, K, dQ, dK
- * [.., d], V, O, dO, dV [.., dv].  (d, dv) is (64, 64), (128, 128) or
- * (192, 128); other pairs return FA_ERR_UNSUPPORTED.  Nq and Nk are limited
+ * [.., d], V, O, dO, dV [.., dv].  (d, dv) is (64, 64), (128, 128),
+ * (256, 256) or (192, 128); other pairs return FA_ERR_UNSUPPORTED.  Nq and Nk are limited
  * to min(FA_MAX_SEQ, 2^30 / max(d, dv)).  bias may be NULL.  Every other
  * argument, ownership, execution and errors as for fa_bwd_masked (the alias
  * checks use each buffer's own extent).

@@ -160,7 +160,7 @@ def call_bwd(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), 1), (dict(do=0), 1), (dict(lse=0), 1), (dict(dq=0), 1), (dict(dk=0), 1), (dict(dl=0), 1),
     (dict(B=-1), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2),
-    (dict(d=96), 3), (dict(d=256), 3), (dict(d=192), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
+    (dict(d=96), 3), (dict(d=32), 3), (dict(d=192), 3), (dict(causal=2), 3), (dict(Nk=(1 << 23) + 1), 3),
     (dict(o=Op2 + 8), 3), (dict(dv=dVp + 4), 3), (dict(dl=Dp + 2), 3),
     (dict(dq=Qp), 4), (dict(dk=Kp + 256), 4), (dict(dv=dKp), 4), (dict(dl=Lp), 4), (dict(dq=dOp + 512), 4),
     (dict(scale=float("nan")), 5),
@@ -206,7 +206,7 @@ def call_bwd_dv(hd=192, hdv=128, **kw):
 
 # extents at B=1, H=2, Nq=Nk=256: Q, K, dQ, dK (d=192) 196608 bytes; V, O, dO, dV (d_v=128) 131072
 @pytest.mark.parametrize("kw,code", [
-    (dict(hd=192, hdv=192), 3), (dict(hd=256, hdv=256), 3), (dict(hd=128, hdv=64), 3), (dict(hd=256, hdv=128), 3),
+    (dict(hd=192, hdv=192), 3), (dict(hd=128, hdv=64), 3), (dict(hd=256, hdv=128), 3), (dict(hd=512, hdv=512), 3),
     (dict(Nk=(1 << 30) // 192 + 1), 3),
     (dict(dq=Kp + 131072), 4),        # inside K only because K rows are 192 wide
     (dict(dl=dOp + 131068), 4),       # last dword of dO (d_v wide)
@@ -379,3 +379,17 @@ def test_mxfp8_quantize_validation_codes():
     assert lib.fa_mxfp8_quantize_vt(Vp, VTp, VSp, 1, 2, 200, 128, 224, None) == 3       # ldv not a multiple of 64
     assert lib.fa_mxfp8_quantize_vt(Vp, VTp, VSp, 1, 2, 300, 128, 256, None) == 3       # ldv < Nk
     assert lib.fa_mxfp8_quantize_vt(Vp, Vp, VSp, 1, 2, 200, 128, 256, None) == 4
+
+
+def test_bwd_head_size_256_reaches_the_device_check():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("would launch on fake pointers")
+    assert call_bwd(d=256) == 6
+    assert call_bwd_dv(hd=256, hdv=256) == 6
+
+
+def test_bwd_head_size_256_rejects_a_bias():
+    assert call_bwd_bias(d=256) == 3
+    assert fa.fa_bwd_dv_raw(Qp, Kp, Vp, Op2, dOp, Lp, dQp, dKp, dVp, Dp, 1, 2, 256, 256, 256, 256, 0.0625, 0,
+                            BIASp, 0, 0, 256, 0) == 3

@@ -274,6 +274,9 @@ HD_CASES = [
     (192, 128, 1, 2, 200, 333, False, "full", 346, "192 / 128, dense bias with -inf keys and an empty row"),
     (192, 128, 1, 2, 200, 333, True, "full", 347, "192 / 128, dense bias, causal"),
     (192, 128, 1, 2, 1, 700, False, None, 348, "192 / 128, one query row"),
+    (256, 256, 1, 2, 256, 256, False, None, 349, "head size 256, tile aligned"),
+    (256, 256, 2, 1, 200, 333, True, None, 350, "head size 256, causal, ragged"),
+    (256, 256, 1, 1, 300, 130, True, None, 351, "head size 256, causal with Nq > Nk"),
 ]
 
 
@@ -298,7 +301,7 @@ def test_bwd_head_sizes_full_compare(fa, d, dv, B, H, Nq, Nk, causal, kind, seed
     assert np.all(got[0][np.isneginf(L)] == 0)
 
 
-@pytest.mark.parametrize("name", ["b2_h32_n8192_d64", "b2_h16_n8192_d192_dv128"])
+@pytest.mark.parametrize("name", ["b2_h32_n8192_d64", "b2_h16_n8192_d192_dv128", "b2_h8_n8192_d256"])
 def test_bwd_head_size_workloads_sampled(fa, name):
     import torch
     w = fi.WORKLOADS[name]
