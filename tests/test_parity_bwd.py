@@ -268,6 +268,9 @@ HD_CASES = [
     (64, 64, 1, 2, 256, 256, False, None, 340, "head size 64, tile aligned"),
     (64, 64, 2, 1, 200, 333, True, None, 341, "head size 64, causal, ragged"),
     (64, 64, 1, 2, 200, 130, False, "per_key_large", 342, "head size 64, per-key bias, ragged"),
+    (64, 64, 1, 2, 200, 333, False, "full", 354, "head size 64, dense bias with -inf keys and an empty row"),
+    (64, 64, 1, 2, 200, 333, True, "full", 355, "head size 64, dense bias, causal"),
+    (64, 64, 2, 2, 300, 300, True, "alibi", 356, "head size 64, ALiBi, causal, several blocks"),
     (192, 128, 1, 2, 256, 256, False, None, 343, "192 / 128, tile aligned"),
     (192, 128, 2, 1, 200, 333, True, None, 344, "192 / 128, causal, ragged"),
     (192, 128, 1, 1, 300, 130, True, None, 345, "192 / 128, causal with Nq > Nk"),
