@@ -34,13 +34,15 @@
 // memory straight into registers; a row whose LSE is -inf (it saw no key)
 // has its -LSE clamped to a large finite value, so -inf bias entries give
 // P = 0 rather than NaN.
-// Both matrix kernels run one wave per SIMD (their accumulators and
-// register-resident operands need ~350 registers), so all overlap of VALU
-// and MFMA work is inside the wave: each step computes two 32-row (or
-// 32-key) sub-blocks, issues the products of the second before the
-// softmax-gradient arithmetic of the first, and sched_group_barrier pins an
-// interleave of one MFMA to a few VALU instructions (6 in dK/dV; 5 and 12
-// in dQ, chosen by timing).
+// At head sizes 128, (192, 128) and 256 both matrix kernels run one wave
+// per SIMD (their accumulators and register-resident operands need ~350 or
+// more registers), so all overlap of VALU and MFMA work is inside the wave:
+// each step computes two 32-row (or 32-key) sub-blocks, issues the products
+// of the second before the softmax-gradient arithmetic of the first, and
+// sched_group_barrier pins an interleave of one MFMA to a few VALU
+// instructions (6 in dK/dV; 5 and 12 in dQ, chosen by timing; not in the dQ
+// kernel at head size 256).  At head size 64 they fit two waves per SIMD.
+// Head size 256 spills to scratch memory and has no bias variant.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
