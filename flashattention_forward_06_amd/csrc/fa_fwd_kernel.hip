@@ -14,7 +14,8 @@
 // accumulator is normalised once after the loop and written.
 //
 // MI355X mapping:
-//   * 4 waves per workgroup, 32 query rows per wave, 2 workgroups per CU.
+//   * 4 waves per workgroup, 32 query rows per wave, 2 workgroups per CU
+//     (3 for the head-size-64 bias variant, 1 at head size 256).
 //   * Scores are produced transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS, Q^T the B operand
 //     held in registers for the whole loop).  The accumulator then gives each
@@ -23,6 +24,8 @@
 //     registers, rounded to bf16, are directly the B operand of
 //     O^T += V^T P^T.  The key order inside an MFMA k-step is permuted
 //     consistently on both operands (the contraction does not depend on it).
+//     At head size 128 the K fragments are read from LDS two k-steps ahead
+//     of the MFMAs that use them.
 //   * V^T fragments come from the row-major V tile in LDS through
 //     ds_read_b64_tr_b16 (a transposing LDS read), so V is never transposed
 //     in memory.
