@@ -36,13 +36,15 @@
 // P = 0 rather than NaN.
 // At head sizes 128, (192, 128) and 256 both matrix kernels run one wave
 // per SIMD (their accumulators and register-resident operands need ~350 or
-// more registers), so all overlap of VALU and MFMA work is inside the wave:
+// more registers; at 256 the dK/dV kernel is launched once per gradient to
+// fit), so all overlap of VALU and MFMA work is inside the wave:
 // each step computes two 32-row (or 32-key) sub-blocks, issues the products
 // of the second before the softmax-gradient arithmetic of the first, and
 // sched_group_barrier pins an interleave of one MFMA to a few VALU
 // instructions (6 in dK/dV; 5 and 12 in dQ, chosen by timing; not in the dQ
 // kernel at head size 256).  At head size 64 they fit two waves per SIMD.
-// Head size 256 spills to scratch memory and has no bias variant.
+// At head size 256 the dQ kernel spills to scratch memory; that size has no
+// bias variant.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -102,8 +104,15 @@ constexpr float NL_MAX = 3.0e38f;
 // K/V or Q/dO operands and the S/dP tiles) and run one wave per SIMD, so the
 // interleave of each wave's own MFMA and VALU work is all the overlap there is.
 constexpr int bwd_waves_per_simd(int dqk) { return dqk == 64 ? 2 : 1; }
+// What one launch of the dK/dV kernel writes: both gradients, or one of them.
+// At head size 256 one wave cannot hold K and V rows and both accumulators
+// (~200 registers spilled); a launch per gradient holds half the
+// accumulators, and the products the other gradient needs are dead code
+// (dV: S and P only; dK: S, dP and dS).  No spills either way: the backward
+// there runs 1.4-1.6x faster although S is computed one more time.
+enum DkdvPart { DKDV_BOTH = 0, DKDV_DV = 1, DKDV_DK = 2 };
 
-template <int DQK, int DV, bool CAUSAL, bool BIAS>
+template <int DQK, int DV, bool CAUSAL, bool BIAS, int PART>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK), bwd_waves_per_simd(DQK))))
 fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -405,10 +414,14 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     }
   }
 
+  if constexpr (PART != DKDV_DV) {
 #pragma unroll
-  for (int cb = 0; cb < NCQ; ++cb) store_bf16_row_block<DQK>(rdk, (uint32_t)key, cb, h, dkacc[cb], scale);
+    for (int cb = 0; cb < NCQ; ++cb) store_bf16_row_block<DQK>(rdk, (uint32_t)key, cb, h, dkacc[cb], scale);
+  }
+  if constexpr (PART != DKDV_DK) {
 #pragma unroll
-  for (int cb = 0; cb < NCV; ++cb) store_bf16_row_block<DV>(rdv, (uint32_t)key, cb, h, dvacc[cb], 1.0f);
+    for (int cb = 0; cb < NCV; ++cb) store_bf16_row_block<DV>(rdv, (uint32_t)key, cb, h, dvacc[cb], 1.0f);
+  }
 }
 
 // ---------------------------------------------------------------- dQ
@@ -639,6 +652,8 @@ struct BwdKernels {
   const void* delta;
   int delta_rows_per_block;
   const void* dkdv[2][2];  // [causal][bias]
+  const void* dkdv_dv[2];  // [causal], no bias: dV only (head size 256)
+  const void* dkdv_dk[2];  // [causal], no bias: dK only (head size 256)
   const void* dq[2][2];
 };
 
@@ -647,8 +662,15 @@ BwdKernels bwd_kernels() {
   BwdKernels k;
   k.delta = (const void*)&fa_bwd_delta_kernel<DV>;
   k.delta_rows_per_block = 256 / (DV / 8);
-  k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false>;
-  k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false>;
+  k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_BOTH>;
+  k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_BOTH>;
+  k.dkdv_dv[0] = k.dkdv_dv[1] = k.dkdv_dk[0] = k.dkdv_dk[1] = nullptr;
+  if constexpr (DQK == 256) {
+    k.dkdv_dv[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DV>;
+    k.dkdv_dv[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DV>;
+    k.dkdv_dk[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DK>;
+    k.dkdv_dk[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DK>;
+  }
   k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false>;
   k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false>;
   // Head size 256 has no bias variant: built with a bias, its dQ kernel
@@ -658,8 +680,8 @@ BwdKernels bwd_kernels() {
   if constexpr (DQK == 256) {
     k.dkdv[0][1] = k.dkdv[1][1] = k.dq[0][1] = k.dq[1][1] = nullptr;
   } else {
-    k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true>;
-    k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true>;
+    k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true, DKDV_BOTH>;
+    k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true, DKDV_BOTH>;
     k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true>;
     k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true>;
   }
@@ -707,9 +729,17 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
     uint16_t* dv = static_cast<uint16_t*>(a.dV);
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
-    if (hipLaunchKernel(kn.dkdv[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
-        hipSuccess)
+    if (kn.dkdv_dv[ci] != nullptr && bi == 0) {
+      // one launch per gradient (head size 256)
+      if (hipLaunchKernel(kn.dkdv_dv[ci], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+              hipSuccess ||
+          hipLaunchKernel(kn.dkdv_dk[ci], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+              hipSuccess)
+        return 1;
+    } else if (hipLaunchKernel(kn.dkdv[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+               hipSuccess) {
       return 1;
+    }
   }
   if (rows > 0) {
     int n_qt = (int)((a.Nq + DQ_ROWS - 1) / DQ_ROWS);
@@ -724,7 +754,8 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 const char* bwd_config_string() {
   return "gfx950 fa_bwd v4: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
-         "(causal at d=128 too); two waves per SIMD at head size 64; head sizes 64, 128, 192/128, 256 (spills); "
+         "(causal at d=128 too); two waves per SIMD at head size 64; one dK/dV launch per gradient at head size 256; "
+         "head sizes 64, 128, 192/128, 256; "
          "fp32 bias; no atomics";
 }
 
