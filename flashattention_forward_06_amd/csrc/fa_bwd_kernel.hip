@@ -43,8 +43,9 @@
 // sched_group_barrier pins an interleave of one MFMA to a few VALU
 // instructions (6 in dK/dV; 5 and 12 in dQ, chosen by timing; not in the dQ
 // kernel at head size 256).  At head size 64 they fit two waves per SIMD.
-// At head size 256 the dQ kernel spills to scratch memory; that size has no
-// bias variant.
+// At head size 256 the dQ kernel is launched once per half of its output
+// columns (each launch recomputes S and dP, holds half the accumulator and
+// spills nothing); that size has no bias variant.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -104,7 +105,8 @@ constexpr float NL_MAX = 3.0e38f;
 // K/V or Q/dO operands and the S/dP tiles) and run one wave per SIMD, so the
 // interleave of each wave's own MFMA and VALU work is all the overlap there is.
 constexpr int bwd_waves_per_simd(int dqk) { return dqk == 64 ? 2 : 1; }
-// What one launch of the dK/dV kernel writes: both gradients, or one of them.
+// What one launch of the dK/dV kernel writes: both gradients, or one of them
+// (QHALF plays the same role for the dQ kernel's output columns).
 // At head size 256 one wave cannot hold K and V rows and both accumulators
 // (~200 registers spilled); a launch per gradient holds half the
 // accumulators, and the products the other gradient needs are dead code
@@ -430,7 +432,7 @@ constexpr int DQ_BC = 64;     // keys per tile
 // LDS: K[2] (rows of 2*DQK bytes), V[2] (2*DV)
 constexpr int dq_lds(int dqk, int dv) { return 2 * DQ_BC * 2 * (dqk + dv); }
 
-template <int DQK, int DV, bool CAUSAL, bool BIAS>
+template <int DQK, int DV, bool CAUSAL, bool BIAS, int QHALF>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(bwd_waves_per_simd(DQK), bwd_waves_per_simd(DQK))))
 fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -444,6 +446,9 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int DQ_TILE_V = DQ_BC * RBV;
   constexpr int NTQ = DQK / 16, NTV = DV / 16;
   constexpr int NCQ = DQK / 32;
+  // output column blocks this launch accumulates and writes: all, or one half
+  constexpr int CB0 = QHALF == 2 ? NCQ / 2 : 0;
+  constexpr int CB1 = QHALF == 1 ? NCQ / 2 : NCQ;
   __shared__ __attribute__((aligned(1024))) char smem[dq_lds(DQK, DV)];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -571,7 +576,7 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
   auto dq_acc = [&](const char* ks, int kb, const bf16x8 (&dsb)[2]) FA_INLINE {
 #pragma unroll
-    for (int cb = 0; cb < NCQ; ++cb)
+    for (int cb = CB0; cb < CB1; ++cb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2)
         dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -581,11 +586,12 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // one tile ahead so its latency hides behind a tile of work; at (192, 128)
   // the registers for that are not there, and each tile loads its own)
   constexpr bool BIAS_AHEAD = DQK + DV <= 256;
-  // Explicit MFMA/VALU interleave of each step.  Not at head size 256: that
-  // build spills ~100 registers to scratch, and with the interleave groups
-  // its dQ came out wrong on the masked tiles (causal diagonal, ragged last
-  // tile) while the unmasked tiles and every other head size were right; the
-  // default schedule of the same source matches the oracle there.
+  // Explicit MFMA/VALU interleave of each step.  Not at head size 256: its
+  // all-columns build spilled ~100 registers to scratch, and with the
+  // interleave groups its dQ came out wrong on the masked tiles (causal
+  // diagonal, ragged last tile) while the unmasked tiles and every other head
+  // size were right; the default schedule of the same source matched the
+  // oracle, and the half-column kernels used at that size keep it.
   constexpr bool DQ_INTERLEAVE = DQK != 256;
   floatx4 bt[2][4], bn[2][4];
   if constexpr (BIAS && BIAS_AHEAD) {
@@ -644,7 +650,7 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   }
 
 #pragma unroll
-  for (int cb = 0; cb < NCQ; ++cb) store_bf16_row_block<DQK>(rdq, (uint32_t)q, cb, h, dqacc[cb], scale);
+  for (int cb = CB0; cb < CB1; ++cb) store_bf16_row_block<DQK>(rdq, (uint32_t)q, cb, h, dqacc[cb], scale);
 }
 
 // Kernels of one (d, d_v) pair.
@@ -654,6 +660,7 @@ struct BwdKernels {
   const void* dkdv[2][2];  // [causal][bias]
   const void* dkdv_dv[2];  // [causal], no bias: dV only (head size 256)
   const void* dkdv_dk[2];  // [causal], no bias: dK only (head size 256)
+  const void* dq_half[2][2];  // [causal][half], no bias: half of the dQ columns (head size 256)
   const void* dq[2][2];
 };
 
@@ -662,17 +669,25 @@ BwdKernels bwd_kernels() {
   BwdKernels k;
   k.delta = (const void*)&fa_bwd_delta_kernel<DV>;
   k.delta_rows_per_block = 256 / (DV / 8);
-  k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_BOTH>;
-  k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_BOTH>;
+  k.dkdv[0][0] = k.dkdv[1][0] = k.dq[0][0] = k.dq[1][0] = nullptr;
   k.dkdv_dv[0] = k.dkdv_dv[1] = k.dkdv_dk[0] = k.dkdv_dk[1] = nullptr;
+  k.dq_half[0][0] = k.dq_half[0][1] = k.dq_half[1][0] = k.dq_half[1][1] = nullptr;
   if constexpr (DQK == 256) {
+    // one launch per gradient for dK/dV, one per half of the columns for dQ
     k.dkdv_dv[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DV>;
     k.dkdv_dv[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DV>;
     k.dkdv_dk[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DK>;
     k.dkdv_dk[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DK>;
+    k.dq_half[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 1>;
+    k.dq_half[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 2>;
+    k.dq_half[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 1>;
+    k.dq_half[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 2>;
+  } else {
+    k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_BOTH>;
+    k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_BOTH>;
+    k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 0>;
+    k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 0>;
   }
-  k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false>;
-  k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false>;
   // Head size 256 has no bias variant: built with a bias, its dQ kernel
   // (about 150 registers spilled to scratch) returned non-finite dQ on every
   // bias layout tested while its dK/dV were right; the entry points reject a
@@ -682,8 +697,8 @@ BwdKernels bwd_kernels() {
   } else {
     k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true, DKDV_BOTH>;
     k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true, DKDV_BOTH>;
-    k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true>;
-    k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true>;
+    k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true, 0>;
+    k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true, 0>;
   }
   return k;
 }
@@ -723,13 +738,14 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   int heads = (int)a.H;
   const int ci = a.causal ? 1 : 0;
   const int bi = bias != nullptr ? 1 : 0;
-  if (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr) return 1;
+  const bool split = kn.dkdv_dv[ci] != nullptr;  // head size 256: no bias variant
+  if (split ? bi != 0 : (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr)) return 1;
   {
     int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
     uint16_t* dv = static_cast<uint16_t*>(a.dV);
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
-    if (kn.dkdv_dv[ci] != nullptr && bi == 0) {
+    if (split) {
       // one launch per gradient (head size 256)
       if (hipLaunchKernel(kn.dkdv_dv[ci], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
               hipSuccess ||
@@ -745,8 +761,16 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
     int n_qt = (int)((a.Nq + DQ_ROWS - 1) / DQ_ROWS);
     uint16_t* dq = static_cast<uint16_t*>(a.dQ);
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dq, &nq, &nk, &n_qt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
-    if (hipLaunchKernel(kn.dq[ci][bi], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) != hipSuccess)
+    if (split) {
+      // one launch per half of the dQ columns (head size 256)
+      for (int hf = 0; hf < 2; ++hf)
+        if (hipLaunchKernel(kn.dq_half[ci][hf], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) !=
+            hipSuccess)
+          return 1;
+    } else if (hipLaunchKernel(kn.dq[ci][bi], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) !=
+               hipSuccess) {
       return 1;
+    }
   }
   return 0;
 }
@@ -754,7 +778,8 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 const char* bwd_config_string() {
   return "gfx950 fa_bwd v4: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
-         "(causal at d=128 too); two waves per SIMD at head size 64; one dK/dV launch per gradient at head size 256; "
+         "(causal at d=128 too); two waves per SIMD at head size 64; at head size 256 one dK/dV launch per gradient "
+         "and one dQ launch per column half; "
          "head sizes 64, 128, 192/128, 256; "
          "fp32 bias; no atomics";
 }

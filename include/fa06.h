@@ -225,16 +225,15 @@ int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t
  *   d        64, 128 (FA_HEAD_DIM) or 256; other values return
  *            FA_ERR_UNSUPPORTED.  At 256 the kernels need more registers
  *            than one wave holds: dK and dV are computed by one launch each
- *            (four kernels in all) and the dQ kernel spills to scratch
- *            memory, so that size runs at about half the rate of the
- *            smaller ones; with a bias (fa_bwd_masked, fa_bwd_dv) it returns
- *            FA_ERR_UNSUPPORTED.
+ *            and dQ by one launch per half of its columns (five kernels in
+ *            all, recomputing S and dP); with a bias (fa_bwd_masked,
+ *            fa_bwd_dv) that size returns FA_ERR_UNSUPPORTED.
  *
  * Requirements and errors as for fa_fwd; every pointer must be 16-byte
  * aligned except LSE and D (4 bytes); an output (dQ, dK, dV, D) that overlaps
  * an input or another output returns FA_ERR_ALIAS.  B*H == 0 is a no-op; with
  * Nq == 0, dK and dV are written as zeros.  The call enqueues three kernels
- * on `stream` (four at head size 256) and is deterministic (no atomics).
+ * on `stream` (five at head size 256) and is deterministic (no atomics).
  */
 int fa_bwd(const void *Q, const void *K, const void *V, const void *O, const void *dO,
            const float *LSE, void *dQ, void *dK, void *dV, float *D,
