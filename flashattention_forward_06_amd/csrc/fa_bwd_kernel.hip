@@ -712,6 +712,11 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   else if (a.d == 192 && a.dv == 128) kn = bwd_kernels<192, 128>();
   else if (a.d == 256 && a.dv == 256) kn = bwd_kernels<256, 256>();
   else return 1;
+  // kernels for this call, checked before anything is enqueued
+  const int ci = a.causal ? 1 : 0;
+  const int bi = a.bias != nullptr ? 1 : 0;
+  const bool split = kn.dkdv_dv[ci] != nullptr;  // head size 256: no bias variant
+  if (split ? bi != 0 : (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr)) return 1;
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
     const int64_t rpb = kn.delta_rows_per_block;
@@ -736,10 +741,6 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   const float* bias = a.bias;
   int64_t sb = a.bias_sb, sh = a.bias_sh, sq = a.bias_sq;
   int heads = (int)a.H;
-  const int ci = a.causal ? 1 : 0;
-  const int bi = bias != nullptr ? 1 : 0;
-  const bool split = kn.dkdv_dv[ci] != nullptr;  // head size 256: no bias variant
-  if (split ? bi != 0 : (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr)) return 1;
   {
     int n_kt = (int)((a.Nk + KV_KEYS - 1) / KV_KEYS);
     uint16_t* dk = static_cast<uint16_t*>(a.dK);
