@@ -40,13 +40,13 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # reads for a plain copy kernel of known size (read x2.000, write x1.000).
 # Reported only while the library's build string is the one measured; any
 # other kernel build reports null.  (The string last changed for the head
-# size 64 bias variant; the head-size-128 kernel measured here compiles to
-# the same machine code.)
+# size 64 bias and (192, 128) variants; the head-size-128 kernel measured
+# here compiles to the same machine code.)
 MEASURED_TRAFFIC = {
     "kernel": "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
               "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on "
-              "mfma_f32_32x32x16_bf16 (K fragments read two k steps ahead at head size 128; three waves per SIMD at "
-              "head size 64 with a bias), V^T via "
+              "mfma_f32_32x32x16_bf16 (K fragments read two k steps ahead at head size 128, one at (192, 128) without "
+              "mask or bias; three waves per SIMD at head size 64 with a bias), V^T via "
               "ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; fp32 additive "
               "bias; key split with LSE merge",
     "workload": "b2_h16_n8192",

@@ -278,10 +278,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // The K fragments of k step t + KPF are read before the MFMAs of step t
   // (a ring of KPF + 1 fragment sets): written in this order, the
   // scheduler keeps the LDS reads further ahead of their use than it does
-  // for a read-then-multiply loop (1.3-1.5 % at head size 128, identical
-  // results).  The other head sizes keep KPF = 0 (read, then multiply):
-  // there the ring costs registers they do not have.
-  constexpr int KPF = DQK == 128 && DV == 128 ? 2 : 0;
+  // for a read-then-multiply loop (1.3-1.5 % at head size 128, 1.2 % at
+  // (192, 128) without mask or bias; identical results).  Elsewhere KPF = 0
+  // (read, then multiply): there the ring costs registers that are not
+  // there (the causal (192, 128) kernel spills more and runs 22 % slower).
+  constexpr int KPF = DQK == 128 && DV == 128 ? 2 : (DQK == 192 && !CAUSAL && !BIAS ? 1 : 0);
   auto scores = [&](const char* ks, floatx16 (&s)[KB]) FA_INLINE {
     auto kfrag = [&](int kb, int t) FA_INLINE {
       return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>(kb * 32 + c, 2 * t + h)));
@@ -787,7 +788,8 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 const char* kernel_config_string() {
   return "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
-         "(K fragments read two k steps ahead at head size 128; three waves per SIMD at head size 64 with a bias), "
+         "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
+         "per SIMD at head size 64 with a bias), "
          "V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; "
          "fp32 additive bias; key split with LSE merge";
 }
