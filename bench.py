@@ -9,9 +9,14 @@ sequence lengths at which the 60 %-of-peak goal is stated.
 
 Prints ONE JSON line: throughput (TFLOP/s, 4*B*H*Nq*Nk*d per call), a
 ``roofline`` object for the kernel (achieved TFLOP/s from HIP events on the
-launch stream vs the MI355X dense-BF16 MFMA peak) and a ``cpu_baseline``
-object (the fp64 oracle timed on a bounded sample of the same workload on
-this host's cores).
+launch stream vs the MI355X dense-BF16 MFMA peak), a ``cpu_baseline`` object
+(the fp64 oracle timed on a bounded sample of the same workload on this
+host's cores; ``all_rows`` says whether the sample is the whole workload),
+``also`` (the 16K workload timed the same way, after the main one), ``clock``
+(the shader clock sampled by a child process during a sustained run after
+the timed region) and ``parity_ok``.  The oracle's rows double as a parity
+check against the forward's gates; if any check fails the line is still
+printed and the process exits with status 3.
 """
 from __future__ import annotations
 
@@ -51,6 +56,7 @@ MEASURED_TRAFFIC = {
               "bias; key split with LSE merge",
     "workload": "b2_h16_n8192",
     "bytes": 340.4e6,
+    "profile": "profiles/fa_fwd_kernel__b2_h16_n8192__hbm_bytes.txt",
 }
 
 
@@ -79,6 +85,12 @@ def parse():
                    help="time the MXFP8 forward (fa_fwd_mxfp8) on the workload's Q, K, V quantized once by the "
                         "library's GPU encoders (not timed); peak = dense FP8 MFMA")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--also", default=None,
+                   help="comma-separated further workloads timed after the main one and reported under "
+                        "'also' (default: the 16K workload when the main one is the default plain forward; "
+                        "'none' for none)")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the sustained run that samples the shader clock")
     p.add_argument("--splitkv", type=int, default=None, metavar="N",
                    help="time the key-split forward (fa_fwd_splitkv, split kernel + merge kernel) with N key "
                         "ranges (0: the library's choice)")
@@ -119,6 +131,102 @@ def visible_pairs(Nq: int, Nk: int, causal: bool) -> int:
     return int(np.clip(i + off + 1, 0, Nk).sum())
 
 
+# Shader-clock sampler, run as a child process (it never touches HIP): reads
+# the GFX clock and socket power through amdsmi every ~20 ms until its stdin
+# closes, then prints one JSON object with the samples.
+CLOCK_SAMPLER = r"""
+import json, sys, threading, time
+out = {"sclk_mhz": [], "power_w": [], "error": None}
+try:
+    import amdsmi
+    amdsmi.amdsmi_init()
+    h = amdsmi.amdsmi_get_processor_handles()[0]
+except Exception as e:  # no amdsmi or no device: report why
+    out["error"] = repr(e)
+    h = None
+stop = threading.Event()
+threading.Thread(target=lambda: (sys.stdin.read(), stop.set()), daemon=True).start()
+print("ready", flush=True)
+while h is not None and not stop.is_set():
+    try:
+        out["sclk_mhz"].append(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.SYS)["clk"])
+    except Exception as e:
+        out["error"] = repr(e)
+    try:
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        p = m.get("current_socket_power", m.get("average_socket_power"))
+        if isinstance(p, (int, float)):
+            out["power_w"].append(p)
+    except Exception:
+        pass
+    time.sleep(0.02)
+print(json.dumps(out), flush=True)
+"""
+
+
+def sustained_clock(step, seconds=1.5):
+    """Runs `step` back to back for about `seconds` while a child process
+    samples the shader clock; returns the median and range of the samples."""
+    import subprocess
+
+    import torch
+    child = subprocess.Popen([sys.executable, "-c", CLOCK_SAMPLER], stdin=subprocess.PIPE,
+                             stdout=subprocess.PIPE, text=True)
+    try:
+        if child.stdout.readline().strip() != "ready":
+            return {"error": "sampler did not start"}
+        t_end = time.perf_counter() + seconds
+        calls = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                step()
+            calls += 8
+            torch.cuda.synchronize()
+        child.stdin.close()
+        res = json.loads(child.stdout.readline() or "{}")
+    finally:
+        child.wait(timeout=30)
+    clk = sorted(res.get("sclk_mhz") or [])
+    pw = sorted(res.get("power_w") or [])
+    if not clk:
+        return {"error": res.get("error") or "no samples", "calls": calls}
+    # skip the first quarter of the samples: the clock settles after the load starts
+    tail = clk[len(clk) // 4:] if len(clk) >= 8 else clk
+    return {"sclk_mhz_median": float(np.median(tail)), "sclk_mhz_min": clk[0], "sclk_mhz_max": clk[-1],
+            "samples": len(clk), "socket_power_w_median": float(np.median(pw)) if pw else None,
+            "seconds": seconds, "calls": calls, "source": "amdsmi GFX clock, child process"}
+
+
+def time_calls(step, stream, steps, warmup):
+    """HIP events on the launch stream around `steps` back-to-back calls after
+    `warmup` untimed ones; returns ms per call."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def metric_name(args, w, bias_kind):
+    """The metric text for the flags actually used; without flags it is the
+    headline metric (forward, bf16, d=128, non-causal)."""
+    dtype = "mxfp8" if args.mxfp8 else "bf16"
+    hd = f"d={w.d}" if w.d == w.d_v else f"d={w.d}, d_v={w.d_v}"
+    mask = "causal" if args.causal else "non-causal"
+    extra = "" if bias_kind == "none" else f", bias {bias_kind}"
+    split = "" if args.splitkv is None else ", key split"
+    peak = "FP8" if args.mxfp8 else ""
+    return (("bwd" if args.bwd else "fwd") + f" attention TFLOP/s ({dtype}, {hd}, {mask}{extra}{split}) and % of "
+            f"MI355X {peak + ' ' if peak else ''}MFMA peak")
+
+
 def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
     import oracle
     import torch
@@ -155,6 +263,9 @@ def cpu_baseline(Q, K, V, w, target_s, o_gpu=None, lse_gpu=None, causal=False):
         "kind": "oracle",
         "sample": f"{n} of {total_rows} query rows of {w.name}{' causal' if causal else ''} "
                   f"(all their visible keys), fp64, {dt:.1f} s",
+        "rows": n,
+        "rows_total": total_rows,
+        "all_rows": n == total_rows,
     }
     parity = None
     if o_gpu is not None:
@@ -304,16 +415,19 @@ def main():
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
+        # HBM bytes per launch taken from the committed counter profile (not
+        # measured in this run); null when the kernel or workload differs
         "traffic": (MEASURED_TRAFFIC["bytes"]
                     if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
                         and not args.mxfp8 and bias is None and args.splitkv is None
                         and w.name == MEASURED_TRAFFIC["workload"]) else None),
+        "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, " + MEASURED_TRAFFIC["profile"]),
         "kernel_ms": round(ev_ms, 4),
         "per_call_ms": {"median": round(float(np.median(per_call)), 4), "min": round(per_call[0], 4),
                         "max": round(per_call[-1], 4), "calls": len(per_call)},
     }
     out = {
-        "metric": ("bwd" if args.bwd else "fwd") + " attention TFLOP/s (bf16, d=128, non-causal) and % of MI355X MFMA peak",
+        "metric": metric_name(args, w, args.bias),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -347,11 +461,66 @@ def main():
         out["roofline"]["note"] = "whole backward call (delta + dK/dV + dQ kernels); per-kernel split in profiles/"
     if args.splitkv is not None:
         out["roofline"]["note"] = f"whole key-split call: split kernel ({n_used} key ranges) + merge kernel"
+    plain = not (args.causal or args.bwd or args.mxfp8 or bias is not None or args.splitkv is not None)
+    if not args.no_clock:
+        out["clock"] = sustained_clock(step)
+    also = args.also
+    if also is None:
+        also = "b1_h16_n16384_koffset" if plain and w.name == DEFAULT_WORKLOAD else "none"
+    failures = []
+    if also != "none":
+        if not plain:
+            raise SystemExit("--also times the plain forward only")
+        out["also"] = {}
+        for name in also.split(","):
+            wa = fi.WORKLOADS[name]
+            Qa, Ka, Va = fi.make_workload(wa)
+            qa, ka, va = up(Qa), up(Ka), up(Va)
+            oa = torch.empty((wa.B, wa.H, wa.Nq, wa.d_v), dtype=torch.bfloat16, device=dev)
+            la = torch.empty((wa.B, wa.H, wa.Nq), dtype=torch.float32, device=dev)
+            a_args = (qa.data_ptr(), ka.data_ptr(), va.data_ptr(), oa.data_ptr(), la.data_ptr(),
+                      wa.B, wa.H, wa.Nq, wa.Nk, wa.d, wa.d_v, wa.scale, 0, None, 0, 0, 0, sptr)
+
+            def step_a():
+                rc = fa.fa_fwd_dv_raw(*a_args)
+                if rc != 0:
+                    raise fa.FaError(rc, fa.fa_status_string(rc))
+
+            ms = time_calls(step_a, stream, args.steps, args.warmup)
+            fl = wa.flops
+            rec = {"TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "frac": round(fl / (ms * 1e-3) / 1e12 / peak, 4),
+                   "kernel_ms": round(ms, 4), "steps": args.steps, "warmup": args.warmup, "flop_per_step": fl}
+            rows = fi.sample_rows(wa.B, wa.H, wa.Nq, 256, seed=wa.seed)
+            import oracle
+            Or, Lr = oracle.attention_rows(Qa, Ka, Va, wa.scale, rows)
+            idx = torch.from_numpy(rows).to(dev)
+            og = oa.view(-1, wa.d_v)[idx].float().cpu().numpy().astype(np.float64)
+            lg = la.view(-1)[idx].cpu().numpy().astype(np.float64)
+            rec["parity_sampled"] = gate({"rows": len(rows), "max_abs_dO": float(np.abs(og - Or).max()),
+                                          "mean_abs_dO": float(np.abs(og - Or).mean()),
+                                          "max_abs_dLSE": float(np.abs(lg - Lr).max())})
+            if not rec["parity_sampled"]["ok"]:
+                failures.append(name)
+            out["also"][name] = rec
+            del qa, ka, va, oa, la
     if not args.no_cpu_baseline and bias is None and not args.bwd and not args.mxfp8:
         cb, parity = cpu_baseline(Q, K, V, w, args.cpu_seconds, o, lse, causal=args.causal)
         out["cpu_baseline"] = cb
-        out["parity_sampled"] = parity
+        out["parity_sampled"] = gate(parity)
+        if not parity["ok"]:
+            failures.append(w.name)
+    out["parity_ok"] = not failures
     print(json.dumps(out), flush=True)
+    if failures:
+        print(f"parity gates failed for {failures}: the throughput above is not valid", file=sys.stderr)
+        sys.exit(3)
+
+
+def gate(p):
+    """Adds the parity verdict (the forward's gates: max|dO| <= 2e-2,
+    mean|dO| <= 2e-3, max|dLSE| <= 1e-3) to a parity record."""
+    p["ok"] = bool(p["max_abs_dO"] <= 2e-2 and p["mean_abs_dO"] <= 2e-3 and p["max_abs_dLSE"] <= 1e-3)
+    return p
 
 
 if __name__ == "__main__":
