@@ -13,6 +13,7 @@ constexpr int NTHREADS = NWAVES * 64;
 constexpr float LOG2E = 1.44269504088896340736f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef short shortx4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef unsigned uintx2 __attribute__((ext_vector_type(2)));

@@ -272,7 +272,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
   for (int i = 0; i < NCB; ++i) oacc[i] = floatx16{};
   float m_run = -__builtin_inff();  // running max, log2 units, per query
-  float l_run = 0.0f;               // partial row sum of this lane's keys
+  float l_run = 0.0f;               // partial row sum of this lane's keys (fp32 P, for LSE)
+  float l_rnd = 0.0f;               // the same over the bf16-rounded P (normalises O)
 
   // S^T = K Q^T for the BC keys of one K buffer (32-key blocks).
   // The K fragments of k step t + KPF are read before the MFMAs of step t
@@ -313,6 +314,26 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[t % (KPF + 1)][kb], qb[t], s[kb], 0, 0, 0);
       }
     }
+  };
+
+  // Row sum of one tile's P as rounded to bf16, i.e. of the weights the P V
+  // product actually uses.  O is divided by this sum, so the weights of every
+  // output row sum to 1 whatever the rounding of P; the fp32 sum of the
+  // unrounded P (l_run) gives the log-sum-exp.  With the running max kept
+  // stale, the largest P of a row is no longer exactly 1 and carries a bf16
+  // rounding error; dividing by the unrounded sum would leave that error
+  // (up to 2^-8 of |v|) in the output.
+  auto rounded_sum = [&](const bf16x8 (&pb)[2 * KB]) FA_INLINE -> float {
+    float acc = 0.0f;
+    const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int i = 0; i < 2 * KB; ++i) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 0, 1), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 2, 3), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 4, 5), one, acc, false);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[i], pb[i], 6, 7), one, acc, false);
+    }
+    return acc;
   };
 
   // Online softmax of one tile's scores -> P (bf16, the B operand of the
@@ -386,6 +407,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     l_run = l_run * alpha + lsum;
+    l_rnd = l_rnd * alpha + rounded_sum(pb);
     return alpha;
   };
 
@@ -424,7 +446,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // the values stay moderate; a lane whose tile sum exceeds 2^16 (or is inf:
   // the first tile, m_run = -inf) sets `fix`, and the caller recomputes the
   // tile with a raised max (slow path, rare).
-  auto softmax_fast = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> bool {
+  auto softmax_fast = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out,
+                          float& lrnd_out) FA_INLINE -> bool {
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -435,10 +458,12 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     lsum_out = lsum;
+    lrnd_out = rounded_sum(pb);
     return __ballot(!(lsum <= 65536.0f)) != 0;
   };
   // slow path of a plain tile: raise the max to the tile's, recompute P
-  auto softmax_fix = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> float {
+  auto softmax_fix = [&](const floatx16 (&s)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out,
+                         float& lrnd_out) FA_INLINE -> float {
     float ext = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -458,6 +483,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     lsum_out = lsum;
+    lrnd_out = rounded_sum(pb);
     return alpha;
   };
 
@@ -466,7 +492,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // only -inf logits so far gives NaN (-inf - -inf), which also sends the
   // tile to the slow path (softmax_fix_logits), where such rows keep P = 0.
   auto softmax_fast_bias = [&](floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB],
-                               float& lsum_out) FA_INLINE -> bool {
+                               float& lsum_out, float& lrnd_out) FA_INLINE -> bool {
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -479,9 +505,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     lsum_out = lsum;
+    lrnd_out = rounded_sum(pb);
     return __ballot(!(lsum <= 65536.0f)) != 0;
   };
-  auto softmax_fix_logits = [&](const floatx16 (&t)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out) FA_INLINE -> float {
+  auto softmax_fix_logits = [&](const floatx16 (&t)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out,
+                                float& lrnd_out) FA_INLINE -> float {
     float ext = t[0][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -502,6 +530,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
     lsum_out = lsum;
+    lrnd_out = rounded_sum(pb);
     return alpha;
   };
 
@@ -559,11 +588,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // spills 11 registers instead of 7 and runs 21 % slower (at the other
     // head sizes the fast path wins by 3-5 %).
     constexpr bool FAST = !decltype(mask1_tag)::value && !(CAUSAL && DQK == 192 && !BIAS);
-    float lsum_f = 0.0f;
+    float lsum_f = 0.0f, lrnd_f = 0.0f;
     bool fix = false;
     if constexpr (HAS_S1) {
-      if constexpr (FAST && BIAS) fix = softmax_fast_bias(s1, bcur, pn, lsum_f);
-      else if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f);
+      if constexpr (FAST && BIAS) fix = softmax_fast_bias(s1, bcur, pn, lsum_f, lrnd_f);
+      else if constexpr (FAST) fix = softmax_fast(s1, pn, lsum_f, lrnd_f);
       else alpha = softmax(s1, bcur, pn, key_lim - (j + 1) * BC, mask1_tag, rs);
     }
     accumulate(vbuf(P), pb);
@@ -572,14 +601,17 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       for (int i = 0; i < 2 * KB; ++i) keep(pn[i]);
       if constexpr (FAST) {
         keep(lsum_f);
+        keep(lrnd_f);
         if (fix) {
-          if constexpr (BIAS) alpha = softmax_fix_logits(s1, pn, lsum_f);
-          else alpha = softmax_fix(s1, pn, lsum_f);
+          if constexpr (BIAS) alpha = softmax_fix_logits(s1, pn, lsum_f, lrnd_f);
+          else alpha = softmax_fix(s1, pn, lsum_f, lrnd_f);
           rs = true;
         }
         l_run = l_run * alpha + lsum_f;
+        l_rnd = l_rnd * alpha + lrnd_f;
       }
       keep(l_run);
+      keep(l_rnd);
       if (rs) rescale_o(alpha);
 #pragma unroll
       for (int i = 0; i < 2 * KB; ++i) pb[i] = pn[i];
@@ -639,10 +671,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
   const float l_tot = wave_sum_halves(l_run);
+  const float l_rnd_tot = wave_sum_halves(l_rnd);
   // l = 0 only for a row that sees no key (causal or all-(-inf) bias):
   // O = 0, LSE = -inf
   constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;
-  const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
+  const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_rnd_tot;
   const int q = q0 + wave * 32 + c;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
