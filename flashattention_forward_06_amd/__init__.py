@@ -26,6 +26,7 @@ STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL_POINTER", 2: "FA_ERR_INVALID_SHAPE", 3: "FA_ERR_UNSUPPORTED",
     4: "FA_ERR_ALIAS", 5: "FA_ERR_INVALID_SCALE", 6: "FA_ERR_DEVICE", 7: "FA_ERR_LAUNCH",
     8: "FA_ERR_WORKSPACE",
+    9: "FA_ERR_SCRATCH",
 }
 
 
@@ -69,6 +70,11 @@ def load_library(path: str | None = None):
     lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
                                    ctypes.c_int, vp, i64, i64, i64, i64, vp, i64, vp]
     lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_float,
+                                           ctypes.c_int, vp, i64, i64, i64, i64, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc_max_bytes.argtypes = []
+    lib.fa_fwd_splitkv_noalloc_max_bytes.restype = ctypes.c_int64
     lib.fa_fwd_splitkv_workspace_bytes.argtypes = [i64, i64, i64, i64, i64, i64, ctypes.POINTER(ctypes.c_int64)]
     lib.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.fa_status_string.argtypes = [ctypes.c_int]
@@ -171,6 +177,21 @@ def fa_fwd_splitkv_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: 
     return load_library().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
                                          ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq,
                                          int(n_splits), ws_ptr, int(ws_bytes), stream)
+
+
+def fa_fwd_splitkv_noalloc_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                               B: int, H: int, Nq: int, Nk: int, d: int, dv: int, scale: float, causal: int,
+                               bias_ptr, sb: int, sh: int, sq: int, n_splits: int, stream: int) -> int:
+    """Direct call of the C ``fa_fwd_splitkv_noalloc`` (partials in the
+    library's scratch array, no allocation); returns the status."""
+    return load_library().fa_fwd_splitkv_noalloc(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Nq, Nk, d, dv,
+                                                 ctypes.c_float(scale), int(causal), bias_ptr, sb, sh, sq,
+                                                 int(n_splits), stream)
+
+
+def splitkv_noalloc_max_bytes() -> int:
+    """Size of the scratch array ``fa_fwd_splitkv_noalloc`` uses."""
+    return int(load_library().fa_fwd_splitkv_noalloc_max_bytes())
 
 
 def splitkv_workspace_bytes(B: int, H: int, Nq: int, Nk: int, dv: int, n_splits: int = 0):
@@ -508,4 +529,5 @@ def fa_fwd_mxfp8(q8, qs, k8, ks, vt8, vs, Nk: int, scale: float | None = None, c
 
 
 __all__ = ["attention", "fa_bwd_dv_raw", "fa_bwd_masked_raw", "fa_fwd_dv_raw", "fa_fwd_mxfp8", "mxfp8_inputs", "mxfp8_quantize_rows", "mxfp8_quantize_vt", "fa_mxfp8_build_info", "fa_bwd", "fa_bwd_raw", "fa_bwd_build_info", "fa_fwd", "fa_fwd_raw", "fa_fwd_masked_raw", "fa_status_string", "fa_build_info", "FaError", "load_library",
-           "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes"]
+           "LIB_PATH", "FA_HEAD_DIM", "FA_MAX_SEQ", "STATUS", "fa_fwd_splitkv_raw", "splitkv_workspace_bytes",
+           "fa_fwd_splitkv_noalloc_raw", "splitkv_noalloc_max_bytes"]

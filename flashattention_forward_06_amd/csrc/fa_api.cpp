@@ -93,7 +93,8 @@ int64_t split_workspace_bytes(const SplitPlan& p, int64_t BH, int64_t Nq, int64_
 int validate_and_launch(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B, int64_t H,
                         int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale, int causal,
                         const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream,
-                        int64_t n_splits = 1, void* workspace = nullptr, int64_t workspace_bytes = 0) {
+                        int64_t n_splits = 1, void* workspace = nullptr, int64_t workspace_bytes = 0,
+                        bool use_scratch = false) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (!head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
   const int64_t dmax = d > dv ? d : dv;
@@ -145,7 +146,10 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
     return FA_ERR_ALIAS;
   // key split: the caller's workspace
   const int64_t ws_need = split_workspace_bytes(plan, BH, Nq, dv);
-  if (plan.n_splits > 1) {
+  if (use_scratch) {
+    // the library's own scratch array stands in for the workspace
+    if (ws_need > fa06::kNoAllocScratchBytes) return FA_ERR_SCRATCH;
+  } else if (plan.n_splits > 1) {
     if (workspace == nullptr || workspace_bytes < ws_need || !aligned(workspace, 16)) return FA_ERR_WORKSPACE;
     if (overlaps(workspace, ws_need, Q, q_bytes) || overlaps(workspace, ws_need, K, k_bytes) ||
         overlaps(workspace, ws_need, V, v_bytes) || overlaps(workspace, ws_need, O, o_bytes) ||
@@ -155,6 +159,7 @@ int validate_and_launch(const void* Q, const void* K, const void* V, void* O, fl
   if (BH * Nq == 0) return FA_OK;
   const int dev = check_device();
   if (dev != FA_OK) return dev;
+  if (use_scratch && plan.n_splits > 1 && fa06::noalloc_scratch(&workspace) != 0) return FA_ERR_DEVICE;
   fa06::LaunchArgs a{};
   a.n_splits = (int)plan.n_splits;
   a.split_keys = (int)plan.split_keys;
@@ -227,6 +232,16 @@ extern "C" int fa_fwd_splitkv(const void* Q, const void* K, const void* V, void*
   return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, dv, scale, causal, bias, bias_stride_b,
                              bias_stride_h, bias_stride_q, stream, n_splits, workspace, workspace_bytes);
 }
+
+extern "C" int fa_fwd_splitkv_noalloc(const void* Q, const void* K, const void* V, void* O, float* LSE, int64_t B,
+                                      int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
+                                      int causal, const float* bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                                      int64_t bias_stride_q, int64_t n_splits, void* stream) {
+  return validate_and_launch(Q, K, V, O, LSE, B, H, Nq, Nk, d, dv, scale, causal, bias, bias_stride_b,
+                             bias_stride_h, bias_stride_q, stream, n_splits, nullptr, 0, true);
+}
+
+extern "C" int64_t fa_fwd_splitkv_noalloc_max_bytes(void) { return fa06::kNoAllocScratchBytes; }
 
 namespace {
 
@@ -461,6 +476,8 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace NULL, smaller than fa_fwd_splitkv_workspace_bytes "
                                   "reports, or not 16-byte aligned";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: fa_fwd_splitkv_noalloc: the key split needs more than the "
+                                "library's scratch array holds (fa_fwd_splitkv_noalloc_max_bytes)";
     default: return "unknown fa_status";
   }
 }

@@ -69,6 +69,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -777,7 +778,30 @@ const void* select_pair(int64_t d, int64_t dv, bool neg, bool causal, bool bias)
   return nullptr;
 }
 
+// Scratch of the no-allocation key split: the ranges' fp32 partial outputs
+// and log-sum-exps of one call, for callers that cannot allocate.  Every
+// device that loads this code object holds its own copy until the process
+// ends.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels and copies take the address noalloc_scratch() returns.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+
 }  // namespace
+
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return 1;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    // once per device, with that device current: the array's address there
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return 1;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return 0;
+}
 
 int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
   const int n_qtiles = (int)((a.Nq + BR - 1) / BR);

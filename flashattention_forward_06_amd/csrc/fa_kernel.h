@@ -30,6 +30,14 @@ struct LaunchArgs {
 
 // Enqueues the kernel; returns 0 or the hipError_t of the launch.
 int launch_fa_fwd(const LaunchArgs& args, hipStream_t stream);
+
+// Size of the per-device scratch array that fa_fwd_splitkv_noalloc uses in
+// place of a caller workspace (the key ranges' fp32 partial outputs and
+// log-sum-exps).
+constexpr int64_t kNoAllocScratchBytes = int64_t(48) << 20;
+// Device address of that array on the current device (looked up once per
+// device, then cached); returns 0, or non-zero if the lookup failed.
+int noalloc_scratch(void** ptr);
 const char* kernel_config_string();
 
 // One backward call over BH = B*H heads, already validated.

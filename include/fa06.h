@@ -48,7 +48,8 @@ typedef enum fa_status {
     FA_ERR_INVALID_SCALE = 5, /* scale is NaN or infinite                          */
     FA_ERR_DEVICE = 6,        /* no HIP device, or the current device is not gfx950 */
     FA_ERR_LAUNCH = 7,        /* the kernel launch itself failed                   */
-    FA_ERR_WORKSPACE = 8      /* fa_fwd_splitkv: workspace NULL, too small or misaligned */
+    FA_ERR_WORKSPACE = 8,     /* fa_fwd_splitkv: workspace NULL, too small or misaligned */
+    FA_ERR_SCRATCH = 9        /* fa_fwd_splitkv_noalloc: the split needs more than the scratch array */
 } fa_status;
 
 /* Head dimension of the headline shape (d = d_v = 128), and the only one the
@@ -189,6 +190,40 @@ int fa_fwd_splitkv(const void *Q, const void *K, const void *V, void *O, float *
                    int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
                    int64_t bias_stride_q, int64_t n_splits, void *workspace, int64_t workspace_bytes,
                    void *stream);
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc): the ranges' partial outputs and log-sum-exps go to
+ * a scratch array inside the library instead of a caller workspace.
+ *
+ *   every argument as for fa_fwd_splitkv, without workspace and
+ *   workspace_bytes.
+ *
+ * Scratch: a static device array of fa_fwd_splitkv_noalloc_max_bytes()
+ * bytes (48 MiB); each device that loads the library's forward kernels holds
+ * its own copy until the process ends.  Its address on a device is looked up
+ * on the first call made with that device current.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).  A plan
+ * that needs more than the array holds (fa_fwd_splitkv_workspace_bytes above
+ * the maximum) returns FA_ERR_SCRATCH and launches nothing; the caller may
+ * ask for fewer ranges.  The array is not cleared: the split kernel writes
+ * every partial row the merge reads.
+ * Concurrency: every call on one device shares that device's array, which
+ * keeps the last call's contents.  Calls that overlap in time on one device
+ * (two streams, or two host threads without ordering) race on it and give
+ * undefined results; calls ordered on one stream are safe.
+ * Errors as for fa_fwd_splitkv, with FA_ERR_WORKSPACE replaced by
+ * FA_ERR_SCRATCH; FA_ERR_DEVICE also when the array's address cannot be
+ * obtained.
+ */
+int fa_fwd_splitkv_noalloc(const void *Q, const void *K, const void *V, void *O, float *LSE,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t dv, float scale,
+                           int causal, const float *bias, int64_t bias_stride_b, int64_t bias_stride_h,
+                           int64_t bias_stride_q, int64_t n_splits, void *stream);
+
+/* fa_fwd_splitkv_noalloc_max_bytes -- size of its scratch array in bytes. */
+int64_t fa_fwd_splitkv_noalloc_max_bytes(void);
 
 /*
  * fa_fwd_splitkv_workspace_bytes -- the workspace fa_fwd_splitkv needs for

@@ -7,6 +7,7 @@
 
 namespace fa06 {
 int launch_fa_fwd(const LaunchArgs&, hipStream_t) { return 1; }
+int noalloc_scratch(void**) { return 1; }
 const char* kernel_config_string() { return "host stub"; }
 int launch_fa_bwd(const BwdArgs&, hipStream_t) { return 1; }
 const char* bwd_config_string() { return "host stub"; }

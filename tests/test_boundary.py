@@ -24,7 +24,8 @@ def test_library_exports_every_declared_function():
     assert names == ["fa_build_info", "fa_bwd", "fa_bwd_build_info", "fa_bwd_dv", "fa_bwd_masked", "fa_fwd",
                      "fa_fwd_dv",
                      "fa_fwd_masked",
-                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_bytes",
+                     "fa_fwd_mxfp8", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_fwd_splitkv_noalloc_max_bytes",
+                     "fa_fwd_splitkv_workspace_bytes",
                      "fa_mxfp8_build_info", "fa_mxfp8_quantize_rows", "fa_mxfp8_quantize_vt", "fa_status_string"]
     for n in names:
         assert hasattr(lib, n), f"{n} declared in fa06.h but not exported"
@@ -341,6 +342,31 @@ def test_split_workspace_rules():
     assert call_split(ws_bytes=need) == 6           # valid: reaches the device check
     assert call_split(ws=0, ws_bytes=0, n=1) == 6   # one range needs no workspace
     assert call_split(ws=0, ws_bytes=0, n=0) == 6   # auto plan of a 256-key problem: one range
+
+
+def test_split_noalloc_rules():
+    """The no-allocation split checks its plan against the scratch array
+    before any HIP call; other arguments follow fa_fwd_splitkv's rules."""
+    cap = fa.splitkv_noalloc_max_bytes()
+    assert cap == 48 << 20
+
+    def call_na(**kw):
+        a = {**GOOD, "dv": GOOD["d"], "causal": 0, "n": 2, **kw}
+        return fa.fa_fwd_splitkv_noalloc_raw(kw.get("q", Qp), kw.get("k", Kp), kw.get("v", Vp), kw.get("o", Op),
+                                             kw.get("lse", Lp), a["B"], a["H"], a["Nq"], a["Nk"], a["d"], a["dv"],
+                                             a["scale"], a["causal"], None, 0, 0, 0, a["n"], 0)
+
+    # 16 heads x 8192 queries x 2 ranges x 516 bytes = 135 MB > 48 MiB
+    need, used = plan(1, 16, 8192, 8192, 128, 2)
+    assert used == 2 and need > cap
+    assert call_na(H=16, Nq=8192, Nk=8192) == 9
+    assert call_na(o=Qp) == 4 and call_na(q=0) == 1 and call_na(n=1025) == 3
+    assert call_na(scale=float("nan")) == 5 and call_na(Nq=0) == 0
+    import torch
+    if torch.cuda.is_available():
+        return
+    assert call_na() == 6                            # fits: reaches the device check
+    assert call_na(n=1) == 6
 
 
 # MXFP8 entry: fake buffers
