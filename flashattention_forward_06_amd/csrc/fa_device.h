@@ -90,16 +90,16 @@ __device__ inline float wave_sum_halves(float x) {
 // swizzle is applied on the source side: the lane that fills physical chunk
 // P of row r loads logical chunk P ^ f(r) (every swizzle is an XOR, its own
 // inverse).  `ROWS` rows starting at global row `row0` (scalar) go to `lds`;
-// every wave issues ROWS*2*DIM/1024/NWAVES instructions.
-template <int ROWS, int S, int DIM = D>
+// each of the workgroup's NW waves issues ROWS*2*DIM/1024/NW instructions.
+template <int ROWS, int S, int DIM = D, int NW = NWAVES>
 __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char* lds, int wave, int lane) {
   constexpr uint32_t RB = 2 * DIM;          // bytes per row
   const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * RB);
-  static_assert(ROWS * (int)RB % (1024 * NWAVES) == 0, "tile must be whole 1 KiB blocks per wave");
-  constexpr int N_INST = ROWS * (int)RB / 1024 / NWAVES;
+  static_assert(ROWS * (int)RB % (1024 * NW) == 0, "tile must be whole 1 KiB blocks per wave");
+  constexpr int N_INST = ROWS * (int)RB / 1024 / NW;
 #pragma unroll
   for (int i = 0; i < N_INST; ++i) {
-    const uint32_t blk = (uint32_t)(i * NWAVES + wave);      // which 1 KiB block
+    const uint32_t blk = (uint32_t)(i * NW + wave);          // which 1 KiB block
     uint32_t row, pos;                                       // pos: physical chunk in the row
     if constexpr ((RB & (RB - 1)) == 0) {
       // whole rows per block: 1024 / RB rows, RB / 16 lanes per row

@@ -14,8 +14,12 @@
 // accumulator is normalised once after the loop and written.
 //
 // MI355X mapping:
-//   * 4 waves per workgroup, 32 query rows per wave, 2 workgroups per CU
-//     (3 for the head-size-64 bias variant, 1 at head size 256).
+//   * 32 query rows per wave.  4 waves per workgroup, 2 workgroups per CU
+//     (3 for the head-size-64 bias variant, 1 at head size 256); for the
+//     plain head-size-128 kernel on grids that fill the chip, 8 waves per
+//     workgroup and 1 workgroup per CU, so each K/V tile copied into LDS
+//     serves 256 query rows (half the copies per FLOP), with the iteration
+//     laid out as 32 fixed segments (below).
 //   * Scores are produced transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16 (K is the A operand from LDS, Q^T the B operand
 //     held in registers for the whole loop).  The accumulator then gives each
@@ -78,7 +82,7 @@
 namespace fa06 {
 namespace {
 
-constexpr int BR = 128;         // query rows per workgroup
+constexpr int BR = 128;         // query rows per 4-wave workgroup (8 waves: 256)
 // LDS: the Q tile (BR rows, staged once) and K and V tiles of BC keys, two of
 // each (K(j+2), K(j+3), V(j), V(j+1)): 64 KiB at head size 128 and BC = 64,
 // 80 KiB at (d, d_v) = (192, 128), either way room for two workgroups per
@@ -110,14 +114,23 @@ constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 //             range only and writes the range's normalised output in fp32
 //             to Opart [n_splits, B*H, Nq, DV] and its log-sum-exp to Lpart
 //             [n_splits, B*H, Nq]; a merge kernel combines the ranges
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT>
-__global__ void __launch_bounds__(NTHREADS)
+//   NW        waves per workgroup: 4, or 8 for the plain head-size-128 kernel
+//             (SEG below), whose workgroups cover 256 query rows
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4>
+__global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(DQK, DV, BIAS), waves_per_simd(DQK, DV, BIAS))))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ LSE,
               const float* __restrict__ bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, int H,
               int Nq, int Nk_all, int n_qtiles, float c_log2, float* __restrict__ Opart,
               float* __restrict__ Lpart, int split_keys, int n_splits) {
+  // SEG: 8 waves share each K/V tile, and plain tiles run the segmented
+  // iteration (iteration_seg): one MFMA per segment, alternately of S(j+2)
+  // and of P(j) V(j)... see there.
+  constexpr bool SEG = NW == 8;
+  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !CAUSAL && !BIAS && !SPLIT),
+                "8-wave workgroups are built for the plain head-size-128 kernel only");
+  constexpr int BR = 32 * NW;                 // query rows per workgroup
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
   constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
   constexpr int RBV = 2 * DV;                 // bytes per V or O row
@@ -125,7 +138,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr int NCB = DV / 32;                // 32-column blocks of the output
   constexpr int K_TILE = BC * RBQ;            // one K tile
   constexpr int V_TILE = BC * RBV;            // one V tile
-  __shared__ __attribute__((aligned(1024))) char smem[lds_bytes(BC, DQK, DV)];
+  __shared__ __attribute__((aligned(1024))) char smem[SEG ? 1024 : lds_bytes(BC, DQK, DV)];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -241,26 +254,51 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // LDS: two K buffers then two V buffers.  K runs two tiles ahead of V:
   // iteration j computes the scores of tile j+2 and accumulates P V of tile
   // j, so K(j+2) and V(j) are read while K(j+3) and V(j+1) are copied in.
-  char* const kbuf0 = smem;
-  char* const vbuf0 = smem + 2 * K_TILE;
-  auto kbuf = [&](int i) FA_INLINE { return kbuf0 + i * K_TILE; };
-  auto vbuf = [&](int i) FA_INLINE { return vbuf0 + i * V_TILE; };
+  // With SEG each buffer is its own LDS array: every loop body reads one
+  // buffer while the LDS-direct copies fill another, and as distinct objects
+  // the compiler can tell that the reads need not wait for those copies.
+  __shared__ __attribute__((aligned(1024))) char seg_k0[SEG ? K_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_k1[SEG ? K_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_v0[SEG ? V_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_v1[SEG ? V_TILE : 16];
+  auto kbuf = [&](int i) FA_INLINE -> char* {
+    if constexpr (SEG) return i ? seg_k1 : seg_k0;
+    else return smem + i * K_TILE;
+  };
+  auto vbuf = [&](int i) FA_INLINE -> char* {
+    if constexpr (SEG) return i ? seg_v1 : seg_v0;
+    else return smem + 2 * K_TILE + i * V_TILE;
+  };
 
   // ---- prologue: the Q tile through LDS into registers.
-  tile_to_lds<BR, SWZ_ROW, DQK>(rq, q0, smem, wave_u, lane);
-  wait_vmem();
-  __syncthreads();
   bf16x8 qb[NT];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
-  {
+  if constexpr (SEG) {
+    // 256 rows in four 64-row pieces, one per K/V buffer
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0, kbuf(0), wave_u, lane);
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0 + 64, kbuf(1), wave_u, lane);
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0 + 128, vbuf(0), wave_u, lane);
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0 + 192, vbuf(1), wave_u, lane);
+    wait_vmem();
+    __syncthreads();
+    const int piece = wave_u >> 1;
+    const char* qs = piece == 0 ? kbuf(0) : piece == 1 ? kbuf(1) : piece == 2 ? vbuf(0) : vbuf(1);
+    const uint32_t row = (wave_u & 1) * 32 + c;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(qs + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
+  } else {
+    tile_to_lds<BR, SWZ_ROW, DQK>(rq, q0, smem, wave_u, lane);
+    wait_vmem();
+    __syncthreads();
     const uint32_t row = wave * 32 + c;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
   }
   __syncthreads();  // the Q staging area is reused from here on
-  tile_to_lds<BC, SWZ_ROW, DQK>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DQK>(rk, BC, kbuf(1), wave_u, lane);
-  tile_to_lds<BC, SWZ_TR, DV>(rv, 0, vbuf(0), wave_u, lane);
+  tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, 0, kbuf(0), wave_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, BC, kbuf(1), wave_u, lane);
+  tile_to_lds<BC, SWZ_TR, DV, NW>(rv, 0, vbuf(0), wave_u, lane);
   floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
   if constexpr (BIAS) {
     load_bias(0, b0);
@@ -557,7 +595,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles > 1) scores(kbuf(1), s1);
   }
   __syncthreads();  // K(0) consumed: K(2) goes into its buffer
-  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DQK>(rk, 2 * BC, kbuf(0), wave_u, lane);
+  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, 2 * BC, kbuf(0), wave_u, lane);
   wait_vmem();
   __syncthreads();
 
@@ -575,8 +613,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
     constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
-    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DV>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DV, NW>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
     if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
     floatx16 s2[KB];
     if constexpr (HAS_S2) scores(kbuf(P), s2);
@@ -631,6 +669,94 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
 
+  // Iteration j on a plain tile with SEG: the same three pieces of work as
+  // `iteration`, in a fixed order of 32 scheduling segments, one MFMA each:
+  // the 16 MFMAs of S(j+2), then the 16 of P(j) V(j) (those run on the V
+  // buffer the copies of this iteration do not touch, and start late, after
+  // the copies have had half an iteration).  Segment i also reads the LDS
+  // operand of the MFMA PF segments later (a ring of PF + 1 fragments per
+  // product) and computes score i + AHEAD of the softmax of tile j+1, which
+  // gives every MFMA about four VALU instructions of the same wave: about as
+  // much VALU work as an MFMA hides (an exponential costs four FMAs, and
+  // about 8 VALU cycles fit under one 32-cycle MFMA).  The compiler still
+  // places the LDS waits, each for a read PF segments old.
+  auto iteration_seg = [&](int j, auto par_tag) FA_INLINE {
+    if constexpr (SEG) {
+    constexpr int P = decltype(par_tag)::value;
+    constexpr int PF = 3, AHEAD = 2;
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
+    tile_to_lds<BC, SWZ_TR, DV, NW>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    const char* ks = kbuf(P);
+    const char* vs = vbuf(P);
+    // MFMA m < 16: S block m & 1, k step m >> 1; MFMA 16 + m: output block
+    // m & 3, keys 16 (m >> 2) .. +15
+    auto kfrag = [&](int m) FA_INLINE {
+      return __builtin_bit_cast(bf16x8,
+                                *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>((m & 1) * 32 + c, 2 * (m >> 1) + h)));
+    };
+    auto vfrag = [&](int m) FA_INLINE { return tr_read_a<SWZ_TR, DV>(vs, (uint32_t)((m >> 2) * 16), m & 3, lane); };
+    floatx16 s2[2];
+    s2[0] = floatx16{};
+    s2[1] = floatx16{};
+    bf16x8 kf[PF + 1], vf[PF + 1], pn[4];
+    float pe[32];
+    float lsum = 0.0f, lrnd = 0.0f;
+    const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
+    auto score = [&](int r) FA_INLINE {  // score r of this lane: key block r >> 4, row r & 15
+      pe[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run));
+      lsum += pe[r];
+    };
+    auto pack = [&](int q) FA_INLINE {  // scores 2q, 2q + 1 -> bf16 (RNE), and their rounded sum
+      const int r = 2 * q;
+      const bf16x2 pr{(__bf16)pe[r], (__bf16)pe[r + 1]};
+      pn[r >> 3][r & 7] = pr[0];
+      pn[r >> 3][(r & 7) + 1] = pr[1];
+      lrnd = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lrnd, false);
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) score(r);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int nxt = i + PF;  // the MFMA whose operand is read in this segment
+      if (nxt < 16) kf[nxt % (PF + 1)] = kfrag(nxt);
+      else if (nxt < 32) vf[(nxt - 16) % (PF + 1)] = vfrag(nxt - 16);
+      if (i + AHEAD < 32) score(i + AHEAD);
+      if (i & 1) pack(i >> 1);
+      if (i < 16) {
+        s2[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qb[i >> 1], s2[i & 1], 0, 0, 0);
+      } else {
+        const int m = i - 16;
+        oacc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m % (PF + 1)], pb[m >> 2], oacc[m & 3], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // a lane's tile sum above 2^16 (or not finite): recompute with the max
+    const bool fix = __ballot(!(lsum <= 65536.0f)) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) keep(pn[i]);
+    keep(lsum);
+    keep(lrnd);
+    float alpha = 1.0f;
+    if (fix) {
+      alpha = softmax_fix(s1, pn, lsum, lrnd);
+      rescale_o(alpha);
+    }
+    l_run = l_run * alpha + lsum;
+    l_rnd = l_rnd * alpha + lrnd;
+    keep(l_run);
+    keep(l_rnd);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = pn[i];
+    s1[0] = s2[0];
+    s1[1] = s2[1];
+    wait_vmem();
+    __syncthreads();
+    }
+  };
+
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using T = std::true_type;
@@ -645,8 +771,13 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       ++j;
     }
     for (; j + 1 < j1; j += 2) {
-      iteration(j, P0{}, T{}, T{}, mask_tag);
-      iteration(j + 1, P1{}, T{}, T{}, mask_tag);
+      if constexpr (SEG && !decltype(mask_tag)::value) {
+        iteration_seg(j, P0{});
+        iteration_seg(j + 1, P1{});
+      } else {
+        iteration(j, P0{}, T{}, T{}, mask_tag);
+        iteration(j + 1, P1{}, T{}, T{}, mask_tag);
+      }
     }
     if (j < j1) iteration(j, P0{}, T{}, T{}, mask_tag);
   };
@@ -747,9 +878,17 @@ fa_fwd_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
   if (t == 0) LSE[r] = m + __log2f(den) * 0.69314718055994530942f;
 }
 
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT>
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4>
 const void* kernel_ptr() {
-  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS, SPLIT>;
+  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS, SPLIT, NW>;
+}
+
+// Grids of the 8-wave kernel: at least one 256-row workgroup per CU (MI355X
+// has 256); smaller launches keep 128-row workgroups, two per CU.
+constexpr int64_t kSegMinWorkgroups = 256;
+bool use_seg(const LaunchArgs& a) {
+  return a.d == 128 && a.dv == 128 && !a.causal && a.bias == nullptr && a.n_splits <= 1 &&
+         a.BH * ((a.Nq + 255) / 256) >= kSegMinWorkgroups;
 }
 
 // Kernel for one pair of head sizes: BC = 64 keys per tile (32 at head size
@@ -804,7 +943,9 @@ int noalloc_scratch(void** ptr) {
 }
 
 int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
-  const int n_qtiles = (int)((a.Nq + BR - 1) / BR);
+  const bool seg = use_seg(a);
+  const int br = seg ? 2 * BR : BR;
+  const int n_qtiles = (int)((a.Nq + br - 1) / br);
   const int64_t nblk = a.BH * n_qtiles;
   const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
   const uint16_t* q = static_cast<const uint16_t*>(a.Q);
@@ -827,10 +968,13 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                   &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
-                         : select_pair<false>(a.d, a.dv, neg, a.causal, b);
+  const void* fn = seg   ? (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8>()
+                                 : kernel_ptr<128, 128, 64, false, false, false, false, 8>())
+                   : split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
+                           : select_pair<false>(a.d, a.dv, neg, a.causal, b);
   if (fn == nullptr) return (int)hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nblk * n_splits)), dim3(NTHREADS), args, 0, stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nblk * n_splits)), dim3(seg ? 2 * NTHREADS : NTHREADS), args, 0,
+                                 stream);
   if (e != hipSuccess || !split) return e == hipSuccess ? 0 : (int)e;
   // merge the key ranges: DV / 4 threads per row
   const int64_t rows = a.BH * a.Nq;
@@ -847,7 +991,8 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+  return "gfx950 fa_fwd v7: BR=128 (4 waves x 32 rows; 256 = 8 waves for plain head size 128 on grids of >= 256 "
+         "workgroups, iteration in 32 fixed MFMA segments), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
          "per SIMD at head size 64 with a bias), "

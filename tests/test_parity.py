@@ -166,6 +166,30 @@ def test_single_hip_runtime(fa):
     assert any("libfa06.so" in ln for ln in maps)
 
 
+# Shapes whose grid holds at least 256 workgroups of 256 query rows
+# (B*H*ceil(Nq/256) >= 256): these run the 8-wave head-size-128 kernel with
+# the segmented iteration.
+SEG_CASES = [
+    # B, H, Nq, Nk, seed, scale, kwargs, note
+    (1, 256, 300, 200, 50, None, {}, "ragged q tile (44 rows) and kv tail (8 keys)"),
+    (2, 128, 256, 1000, 51, None, {}, "seven segmented iteration pairs, ragged kv"),
+    (1, 256, 1, 64, 52, None, {}, "one query row per head, one kv tile"),
+    (1, 256, 256, 640, 53, -0.0883883476, {}, "negative scale"),
+    (1, 256, 256, 1024, 54, None, dict(k_scale=4.0, offset_frac=0.01, offset=8.0),
+     "large logits, running-max jumps (the 16K workload's recipe)"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,scale,kw,note", SEG_CASES)
+def test_eight_wave_kernel_full_compare(fa, B, H, Nq, Nk, seed, scale, kw, note):
+    say(f"case 8-wave B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed, **kw)
+    sc = 1.0 / math.sqrt(128) if scale is None else scale
+    Og, Lg = run_gpu(fa, Q, K, V, sc)
+    Oo, Lo = oracle.attention(Q, K, V, sc)
+    check_parity(Og, Lg, Oo, Lo, f"8-wave {note}")
+
+
 CAUSAL_CASES = [
     # B, H, Nq, Nk, seed, note
     (1, 2, 256, 256, 80, "square, tile aligned"),
