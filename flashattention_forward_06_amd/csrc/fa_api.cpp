@@ -245,10 +245,9 @@ extern "C" int64_t fa_fwd_splitkv_noalloc_max_bytes(void) { return fa06::kNoAllo
 
 namespace {
 
-// (d, dv) pairs with backward kernels.  At head size 256 the kernels keep
-// more in registers than one wave holds (K and V rows and both accumulators
-// in the dK/dV kernel): they run, with spills to scratch memory, and without
-// a bias.
+// (d, dv) pairs with backward kernels.  At head size 256 the dK/dV kernel
+// runs once per gradient and the dQ kernel once per half of its columns, so
+// that each fits one wave's registers.
 bool bwd_head_sizes_supported(int64_t d, int64_t dv) {
   return (d == dv && (d == 64 || d == 128 || d == 256)) || (d == 192 && dv == 128);
 }
@@ -259,7 +258,6 @@ int bwd_validate_and_launch(const void* Q, const void* K, const void* V, const v
                             const float* bias, int64_t bias_sb, int64_t bias_sh, int64_t bias_sq, void* stream) {
   if (B < 0 || H < 0 || Nq < 0 || Nk < 1) return FA_ERR_INVALID_SHAPE;
   if (!bwd_head_sizes_supported(d, dv)) return FA_ERR_UNSUPPORTED;
-  if (d == 256 && bias != nullptr) return FA_ERR_UNSUPPORTED;  // no bias kernels at head size 256
   const int64_t dmax = d > dv ? d : dv;
   if (Nq > max_seq(dmax) || Nk > max_seq(dmax)) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;

@@ -44,8 +44,8 @@
 // instructions (6 in dK/dV; 5 and 12 in dQ, chosen by timing; not in the dQ
 // kernel at head size 256).  At head size 64 they fit two waves per SIMD.
 // At head size 256 the dQ kernel is launched once per half of its output
-// columns (each launch recomputes S and dP, holds half the accumulator and
-// spills nothing); that size has no bias variant.
+// columns and the dK/dV kernel once per gradient (each launch recomputes S
+// and dP as it needs them and spills nothing), with or without a bias.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -657,46 +657,50 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 struct BwdKernels {
   const void* delta;
   int delta_rows_per_block;
-  const void* dkdv[2][2];  // [causal][bias]
-  const void* dkdv_dv[2];  // [causal], no bias: dV only (head size 256)
-  const void* dkdv_dk[2];  // [causal], no bias: dK only (head size 256)
-  const void* dq_half[2][2];  // [causal][half], no bias: half of the dQ columns (head size 256)
+  const void* dkdv[2][2];        // [causal][bias]
+  const void* dkdv_dv[2][2];     // [causal][bias]: dV only (head size 256)
+  const void* dkdv_dk[2][2];     // [causal][bias]: dK only (head size 256)
+  const void* dq_half[2][2][2];  // [causal][bias][half]: half of the dQ columns (head size 256)
   const void* dq[2][2];
+  bool split;                    // head size 256: the split kernels above
 };
 
 template <int DQK, int DV>
 BwdKernels bwd_kernels() {
-  BwdKernels k;
+  BwdKernels k{};
   k.delta = (const void*)&fa_bwd_delta_kernel<DV>;
   k.delta_rows_per_block = 256 / (DV / 8);
-  k.dkdv[0][0] = k.dkdv[1][0] = k.dq[0][0] = k.dq[1][0] = nullptr;
-  k.dkdv_dv[0] = k.dkdv_dv[1] = k.dkdv_dk[0] = k.dkdv_dk[1] = nullptr;
-  k.dq_half[0][0] = k.dq_half[0][1] = k.dq_half[1][0] = k.dq_half[1][1] = nullptr;
+  k.split = DQK == 256;
   if constexpr (DQK == 256) {
-    // one launch per gradient for dK/dV, one per half of the columns for dQ
-    k.dkdv_dv[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DV>;
-    k.dkdv_dv[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DV>;
-    k.dkdv_dk[0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DK>;
-    k.dkdv_dk[1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DK>;
-    k.dq_half[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 1>;
-    k.dq_half[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 2>;
-    k.dq_half[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 1>;
-    k.dq_half[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 2>;
+    // one launch per gradient for dK/dV, one per half of the columns for dQ.
+    // Each fits one wave's registers without spilling to scratch memory.
+    // The all-in-one kernels at this size spilled 100-150 registers to
+    // scratch, and two of those builds (the dQ kernel with explicit
+    // interleave groups; the dQ kernel with a bias) returned wrong dQ while
+    // the same source compiled without scratch spills matches the oracle.
+    k.dkdv_dv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DV>;
+    k.dkdv_dv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DV>;
+    k.dkdv_dv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true, DKDV_DV>;
+    k.dkdv_dv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true, DKDV_DV>;
+    k.dkdv_dk[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_DK>;
+    k.dkdv_dk[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_DK>;
+    k.dkdv_dk[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true, DKDV_DK>;
+    k.dkdv_dk[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true, DKDV_DK>;
+    k.dq_half[0][0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 1>;
+    k.dq_half[0][0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 2>;
+    k.dq_half[1][0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 1>;
+    k.dq_half[1][0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 2>;
+    k.dq_half[0][1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true, 1>;
+    k.dq_half[0][1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true, 2>;
+    k.dq_half[1][1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true, 1>;
+    k.dq_half[1][1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true, 2>;
   } else {
     k.dkdv[0][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, false, DKDV_BOTH>;
     k.dkdv[1][0] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, false, DKDV_BOTH>;
-    k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 0>;
-    k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 0>;
-  }
-  // Head size 256 has no bias variant: built with a bias, its dQ kernel
-  // (about 150 registers spilled to scratch) returned non-finite dQ on every
-  // bias layout tested while its dK/dV were right; the entry points reject a
-  // bias at that size instead.
-  if constexpr (DQK == 256) {
-    k.dkdv[0][1] = k.dkdv[1][1] = k.dq[0][1] = k.dq[1][1] = nullptr;
-  } else {
     k.dkdv[0][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, false, true, DKDV_BOTH>;
     k.dkdv[1][1] = (const void*)&fa_bwd_dkdv_kernel<DQK, DV, true, true, DKDV_BOTH>;
+    k.dq[0][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, false, 0>;
+    k.dq[1][0] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, false, 0>;
     k.dq[0][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, false, true, 0>;
     k.dq[1][1] = (const void*)&fa_bwd_dq_kernel<DQK, DV, true, true, 0>;
   }
@@ -715,8 +719,11 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
   // kernels for this call, checked before anything is enqueued
   const int ci = a.causal ? 1 : 0;
   const int bi = a.bias != nullptr ? 1 : 0;
-  const bool split = kn.dkdv_dv[ci] != nullptr;  // head size 256: no bias variant
-  if (split ? bi != 0 : (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr)) return 1;
+  const bool split = kn.split;
+  if (split ? (kn.dkdv_dv[ci][bi] == nullptr || kn.dkdv_dk[ci][bi] == nullptr || kn.dq_half[ci][bi][0] == nullptr ||
+               kn.dq_half[ci][bi][1] == nullptr)
+            : (kn.dkdv[ci][bi] == nullptr || kn.dq[ci][bi] == nullptr))
+    return 1;
   const int64_t rows = a.BH * a.Nq;
   if (rows > 0) {
     const int64_t rpb = kn.delta_rows_per_block;
@@ -748,9 +755,9 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
     void* args[] = {&q, &k, &v, &g, &lse, &dl, &dk, &dv, &nq, &nk, &n_kt, &cl, &sc, &bias, &sb, &sh, &sq, &heads};
     if (split) {
       // one launch per gradient (head size 256)
-      if (hipLaunchKernel(kn.dkdv_dv[ci], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+      if (hipLaunchKernel(kn.dkdv_dv[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
               hipSuccess ||
-          hipLaunchKernel(kn.dkdv_dk[ci], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
+          hipLaunchKernel(kn.dkdv_dk[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
               hipSuccess)
         return 1;
     } else if (hipLaunchKernel(kn.dkdv[ci][bi], dim3((unsigned)(a.BH * n_kt)), dim3(NTHREADS), args, 0, stream) !=
@@ -765,7 +772,7 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
     if (split) {
       // one launch per half of the dQ columns (head size 256)
       for (int hf = 0; hf < 2; ++hf)
-        if (hipLaunchKernel(kn.dq_half[ci][hf], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) !=
+        if (hipLaunchKernel(kn.dq_half[ci][bi][hf], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) !=
             hipSuccess)
           return 1;
     } else if (hipLaunchKernel(kn.dq[ci][bi], dim3((unsigned)(a.BH * n_qt)), dim3(NTHREADS), args, 0, stream) !=
@@ -777,10 +784,10 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 }
 
 const char* bwd_config_string() {
-  return "gfx950 fa_bwd v4: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
+  return "gfx950 fa_bwd v5: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
          "(causal at d=128 too); two waves per SIMD at head size 64; at head size 256 one dK/dV launch per gradient "
-         "and one dQ launch per column half; "
+         "and one dQ launch per column half (bias too); "
          "head sizes 64, 128, 192/128, 256; "
          "fp32 bias; no atomics";
 }

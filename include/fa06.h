@@ -261,8 +261,7 @@ int64_t fa_fwd_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t
  *            FA_ERR_UNSUPPORTED.  At 256 the kernels need more registers
  *            than one wave holds: dK and dV are computed by one launch each
  *            and dQ by one launch per half of its columns (five kernels in
- *            all, recomputing S and dP); with a bias (fa_bwd_masked,
- *            fa_bwd_dv) that size returns FA_ERR_UNSUPPORTED.
+ *            all, recomputing S and dP), with or without a bias.
  *
  * Requirements and errors as for fa_fwd; every pointer must be 16-byte
  * aligned except LSE and D (4 bytes); an output (dQ, dK, dV, D) that overlaps

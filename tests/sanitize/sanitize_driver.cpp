@@ -177,8 +177,8 @@ static void check_backward_validation() {
   EXPECT(fa_bwd(q.data(), k.data(), v.data(), o.data(), dO.data(), lse.data(), dq.data(), dq.data(), dv.data(),
                 D.data(), B, H, Nq, Nk, d, sc, 0, nullptr) == FA_ERR_ALIAS, "dK aliases dQ");
   EXPECT(fa_bwd_masked(q.data(), k.data(), v.data(), o.data(), dO.data(), lse.data(), dq.data(), dk.data(),
-                       dv.data(), D.data(), B, H, Nq, Nk, 256, sc, 0, bias.data(), H * Nk, Nk, 0, nullptr) ==
-             FA_ERR_UNSUPPORTED, "bias at head size 256");
+                       dv.data(), D.data(), B, H, Nq, Nk, 96, sc, 0, bias.data(), H * Nk, Nk, 0, nullptr) ==
+             FA_ERR_UNSUPPORTED, "bias backward at head size 96");
   EXPECT(fa_bwd_dv(q.data(), k.data(), v.data(), o.data(), dO.data(), lse.data(), dq.data(), dk.data(), dv.data(),
                    D.data(), B, H, Nq, Nk, d, d, sc, 3, nullptr, 0, 0, 0, nullptr) == FA_ERR_UNSUPPORTED,
          "bwd causal flag 3");

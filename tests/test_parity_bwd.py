@@ -280,6 +280,11 @@ HD_CASES = [
     (256, 256, 1, 2, 256, 256, False, None, 349, "head size 256, tile aligned"),
     (256, 256, 2, 1, 200, 333, True, None, 350, "head size 256, causal, ragged"),
     (256, 256, 1, 1, 300, 130, True, None, 351, "head size 256, causal with Nq > Nk"),
+    (256, 256, 1, 2, 200, 333, False, "full", 357, "head size 256, dense bias with -inf keys and an empty row"),
+    (256, 256, 1, 2, 200, 333, True, "full", 358, "head size 256, dense bias, causal, ragged"),
+    (256, 256, 1, 2, 200, 130, False, "per_key_large", 359, "head size 256, per-key bias with +60 entries"),
+    (256, 256, 2, 2, 300, 300, True, "alibi", 360, "head size 256, ALiBi, causal, several blocks"),
+    (256, 256, 3, 2, 300, 333, False, "batch_shared", 361, "head size 256, [1,H,Nq,Nk] over 3 batches"),
 ]
 
 
