@@ -44,18 +44,17 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # (one run each) on the default workload, each scaled by what the same counter
 # reads for a plain copy kernel of known size (read x2.000, write x1.000).
 # Reported only while the library's build string is the one measured; any
-# other kernel build reports null.  (The string last changed for the head
-# size 64 bias and (192, 128) variants; the head-size-128 kernel measured
-# here compiles to the same machine code.)
+# other kernel build reports null.
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v6: BR=128 (4 waves x 32 rows), BC=64 (32 with bias), 3-stage K/V pipeline "
+    "kernel": "gfx950 fa_fwd v7: BR=128 (4 waves x 32 rows; 256 = 8 waves for plain head size 128 on grids of "
+              ">= 256 workgroups, iteration in 32 fixed MFMA segments), BC=64 (32 with bias), 3-stage K/V pipeline "
               "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on "
               "mfma_f32_32x32x16_bf16 (K fragments read two k steps ahead at head size 128, one at (192, 128) without "
               "mask or bias; three waves per SIMD at head size 64 with a bias), V^T via "
               "ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; fp32 additive "
               "bias; key split with LSE merge",
     "workload": "b2_h16_n8192",
-    "bytes": 340.4e6,
+    "bytes": 269.8e6,
     "profile": "profiles/fa_fwd_kernel__b2_h16_n8192__hbm_bytes.txt",
 }
 
@@ -409,19 +408,21 @@ def main():
     value = flop / (ms_per_step * 1e-3) / 1e12
     achieved = flop / (ev_ms * 1e-3) / 1e12
     peak = MFMA_FP8_PEAK_TFLOPS if args.mxfp8 else MFMA_BF16_PEAK_TFLOPS
+    # HBM bytes per launch taken from the committed counter profile (not
+    # measured in this run); null when the kernel or workload differs
+    traffic = (MEASURED_TRAFFIC["bytes"]
+               if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
+                   and not args.mxfp8 and bias is None and args.splitkv is None
+                   and w.name == MEASURED_TRAFFIC["workload"]) else None)
     roof = {
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": peak,
         "unit": "TFLOP/s",
         "frac": round(achieved / peak, 4),
-        # HBM bytes per launch taken from the committed counter profile (not
-        # measured in this run); null when the kernel or workload differs
-        "traffic": (MEASURED_TRAFFIC["bytes"]
-                    if (fa.fa_build_info() == MEASURED_TRAFFIC["kernel"] and not args.causal and not args.bwd
-                        and not args.mxfp8 and bias is None and args.splitkv is None
-                        and w.name == MEASURED_TRAFFIC["workload"]) else None),
-        "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, " + MEASURED_TRAFFIC["profile"]),
+        "traffic": traffic,
+        "traffic_source": ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, " + MEASURED_TRAFFIC["profile"]
+                           if traffic is not None else "not measured for this kernel build and workload"),
         "kernel_ms": round(ev_ms, 4),
         "per_call_ms": {"median": round(float(np.median(per_call)), 4), "min": round(per_call[0], 4),
                         "max": round(per_call[-1], 4), "calls": len(per_call)},
