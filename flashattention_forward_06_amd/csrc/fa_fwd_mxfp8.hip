@@ -19,9 +19,14 @@
 // the byte of the 32-bit scale register).  The output is the usual
 // D[8(q/4) + 4g + q%4][r] for accumulator register q.
 //
-// Loop structure: as the bf16 kernel (one workgroup per 128 query rows, 4
-// waves of 32, 64-key tiles, three-stage pipeline: S of tile j+2 and P V of
-// tile j on the MFMAs with the softmax of tile j+1 in between).  S^T = K Q^T
+// Loop structure: as the bf16 kernel (waves of 32 query rows, 64-key tiles,
+// three-stage pipeline: S of tile j+2 and P V of tile j on the MFMAs with the
+// softmax of tile j+1 in between).  Workgroups have 8 waves (256 rows, one
+// workgroup per CU, each K/V tile shared by twice the rows) on grids of at
+// least 256 such workgroups and 4 waves (128 rows, two per CU) otherwise.
+// Plain tiles run the iteration in a fixed order of 8 segments, one MFMA
+// each, with the softmax scores and operand reads spread over them
+// (iteration_seg); masked tiles keep the compiler-scheduled iteration.  S^T = K Q^T
 // reads the K tile's rows in a permuted order so that each lane's 16
 // accumulator rows are 16 consecutive keys: the two 32-key blocks of a tile
 // then give each lane exactly the key bytes the P operand of the 64-key P V
@@ -40,7 +45,6 @@ namespace {
 
 typedef int intx8 __attribute__((ext_vector_type(8)));
 
-constexpr int MX_BR = 128;             // query rows per workgroup
 constexpr int MX_BC = 64;              // keys per tile
 constexpr int MX_KROW = 128;           // bytes per K row (d = 128 E4M3 elements)
 constexpr int MX_KTILE = MX_BC * MX_KROW;        // 8 KiB
@@ -70,8 +74,8 @@ __device__ inline intx8 lds_read32(const char* p0, const char* p1) {
   return intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-template <bool NEG_SCALE, bool CAUSAL>
-__global__ void __launch_bounds__(NTHREADS)
+template <bool NEG_SCALE, bool CAUSAL, int NW>
+__global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ Qs,
                     const uint8_t* __restrict__ K8, const uint8_t* __restrict__ Ks,
@@ -79,6 +83,7 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
                     uint16_t* __restrict__ O, float* __restrict__ LSE,
                     int Nq, int Nk, int ldv, int n_qtiles, float c_log2) {
   constexpr int KB = 2;  // 32-key blocks per tile
+  constexpr int BR = 32 * NW;  // query rows per workgroup
   __shared__ __attribute__((aligned(1024))) char smem[MX_LDS];
 
   const int tid = threadIdx.x;
@@ -99,7 +104,7 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     bh = bid / n_qtiles;
     qt = bid - bh * n_qtiles;
   }
-  const int q0 = qt * MX_BR;
+  const int q0 = qt * BR;
 
   const size_t bq = (size_t)bh * (size_t)Nq, bk = (size_t)bh * (size_t)Nk;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q8 + bq * D, (uint32_t)Nq * D);
@@ -118,7 +123,7 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   const int q = q0 + wave * 32 + c;
   if constexpr (CAUSAL) {
     const int off = Nk - Nq;
-    const int q_last = (q0 + MX_BR < Nq ? q0 + MX_BR : Nq) - 1;
+    const int q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;
     const int lim_last = q_last + off;
     const int lim_first = q0 + off;
     const int need = lim_last < 0 ? 0 : lim_last / MX_BC + 1;
@@ -147,8 +152,8 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   auto k_to_lds = [&](int j, char* dst) FA_INLINE {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)MX_KTILE);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t blk = (uint32_t)(i * NWAVES + wave_u);  // 1 KiB = 8 rows
+    for (int i = 0; i < 8 / NW; ++i) {
+      const uint32_t blk = (uint32_t)(i * NW + wave_u);  // 1 KiB = 8 rows
       const uint32_t row = blk * 8u + ((uint32_t)lane >> 3);
       const uint32_t ch = ((uint32_t)lane & 7u) ^ kx(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)((lds_char*)dst + blk * 1024u),
@@ -164,8 +169,8 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   auto v_to_lds = [&](int j, char* dst) FA_INLINE {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)MX_BC);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t blk = (uint32_t)(i * NWAVES + wave_u);  // 1 KiB = 16 rows
+    for (int i = 0; i < 8 / NW; ++i) {
+      const uint32_t blk = (uint32_t)(i * NW + wave_u);  // 1 KiB = 16 rows
       const uint32_t row = blk * 16u + ((uint32_t)lane >> 2);
       const uint32_t ch = ((uint32_t)lane & 3u) ^ vx(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)((lds_char*)dst + blk * 1024u),
@@ -405,6 +410,93 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
     }
   };
 
+  // Iteration j on a plain tile in a fixed order of 8 scheduling segments,
+  // one MFMA each: the 4 of S(j+2) (key block m >> 1, head-dimension slab
+  // m & 1), then the 4 of P(j) V(j) (output block m - 4).  Segment i also
+  // reads the LDS operand (and scale) of the MFMA PF segments later and
+  // computes 4 scores of the softmax of tile j+1 (AHEAD scores in advance),
+  // packing the four it has finished into E4M3.
+  auto iteration_seg = [&](int j, auto par_tag) FA_INLINE {
+    constexpr int P = decltype(par_tag)::value;
+    // measured best: PF 2 with 6 scores ahead at 8 waves, 4 ahead at 4 waves
+    constexpr int PF = 2, AHEAD = NW == 8 ? 6 : 4;
+    if (j + 3 < n_tiles) k_to_lds(j + 3, kbuf(P ^ 1));
+    v_to_lds(j + 1, vbuf(P ^ 1));
+    const char* ks = kbuf(P);
+    const char* vs = vbuf(P);
+    auto afrag = [&](int m, int& sc) FA_INLINE -> intx8 {
+      if (m < 4) {
+        const uint32_t row = (uint32_t)(m >> 1) * 32u + key_of_row((uint32_t)c);
+        const char* rp = ks + row * MX_KROW;
+        const uint32_t t4 = 4u * (uint32_t)(m & 1);
+        sc = (int)(*reinterpret_cast<const uint32_t*>(ks + MX_KTILE + row * 4u) >> (8 * h));
+        return lds_read32(rp + (((t4 + (uint32_t)h) ^ kx(row)) << 4), rp + (((t4 + 2u + (uint32_t)h) ^ kx(row)) << 4));
+      }
+      const uint32_t row = (uint32_t)((m - 4) * 32 + c);
+      const char* rp = vs + row * MX_VROW;
+      sc = (int)*reinterpret_cast<const uint8_t*>(vs + MX_VTILE + h * D + row);
+      return lds_read32(rp + (((uint32_t)h ^ vx(row)) << 4), rp + (((2u + (uint32_t)h) ^ vx(row)) << 4));
+    };
+    floatx16 s2[KB];
+    s2[0] = floatx16{};
+    s2[1] = floatx16{};
+    intx8 af[PF + 1];
+    int asc[PF + 1];
+    float pe[32];
+    intx8 pn;
+    float lsum = 0.0f;
+    auto score = [&](int r) FA_INLINE {  // key block r >> 4, accumulator row r & 15
+      pe[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run));
+      lsum += pe[r];
+    };
+    auto pack = [&](int w) FA_INLINE {  // scores 4w .. 4w+3 -> B operand word w
+      int v = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w], pe[4 * w + 1], 0, false);
+      v = __builtin_amdgcn_cvt_pk_fp8_f32(pe[4 * w + 2], pe[4 * w + 3], v, true);
+      pn[w] = v;
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) af[i] = afrag(i, asc[i]);
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) score(r);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int nxt = i + PF;
+      if (nxt < 8) af[nxt % (PF + 1)] = afrag(nxt, asc[nxt % (PF + 1)]);
+#pragma unroll
+      for (int r = 4 * i + AHEAD; r < 4 * i + 4 + AHEAD; ++r)
+        if (r < 32) score(r);
+      pack(i);
+      const int slot = i % (PF + 1);
+      if (i < 4) {
+        const int kb = i >> 1;
+        if (i & 1)
+          s2[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[slot], qf[1], s2[kb], 0, 0, 2, asc[slot], 2, qsw);
+        else
+          s2[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[slot], qf[0], s2[kb], 0, 0, 0, asc[slot], 0, qsw);
+      } else {
+        oacc[i - 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[slot], pb, oacc[i - 4], 0, 0, 0, asc[slot], 0,
+                                                                       0x7F7F7F7F);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bool fix = __ballot(!(lsum <= 256.0f)) != 0;
+    asm volatile("" ::"v"(pn));
+    keep(lsum);
+    float alpha = 1.0f;
+    if (fix) {
+      alpha = softmax_fix(s1, pn, lsum);
+      rescale_o(alpha);
+    }
+    l_run = l_run * alpha + lsum;
+    keep(l_run);
+    pb = pn;
+    s1[0] = s2[0];
+    s1[1] = s2[1];
+    wait_vmem();
+    __syncthreads();
+  };
+
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
   using T = std::true_type;
@@ -416,8 +508,13 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
       ++j;
     }
     for (; j + 1 < j1; j += 2) {
-      iteration(j, P0{}, T{}, T{}, mask_tag);
-      iteration(j + 1, P1{}, T{}, T{}, mask_tag);
+      if constexpr (!decltype(mask_tag)::value) {
+        iteration_seg(j, P0{});
+        iteration_seg(j + 1, P1{});
+      } else {
+        iteration(j, P0{}, T{}, T{}, mask_tag);
+        iteration(j + 1, P1{}, T{}, T{}, mask_tag);
+      }
     }
     if (j < j1) iteration(j, P0{}, T{}, T{}, mask_tag);
   };
@@ -541,8 +638,14 @@ __global__ void __launch_bounds__(256) mx_quantize_vt_kernel(const uint16_t* __r
 
 }  // namespace
 
-int launch_fa_fwd_mxfp8(const MxArgs& a, hipStream_t stream) {
-  int n_qtiles = (int)((a.Nq + MX_BR - 1) / MX_BR);
+// Workgroups of 8 waves (256 query rows) share each K/V tile between twice
+// the rows; they pay on grids that still give every CU a workgroup of them.
+constexpr int64_t kMx8WaveMinWorkgroups = 256;
+
+namespace {
+template <int NW>
+int launch_mxfp8_nw(const MxArgs& a, hipStream_t stream) {
+  int n_qtiles = (int)((a.Nq + 32 * NW - 1) / (32 * NW));
   const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
   const uint8_t *q = static_cast<const uint8_t*>(a.Q8), *qs = static_cast<const uint8_t*>(a.Qs);
   const uint8_t *k = static_cast<const uint8_t*>(a.K8), *ks = static_cast<const uint8_t*>(a.Ks);
@@ -553,10 +656,17 @@ int launch_fa_fwd_mxfp8(const MxArgs& a, hipStream_t stream) {
   float cl = c_log2;
   void* args[] = {&q, &qs, &k, &ks, &v, &vs, &o, &lse, &nq, &nk, &ldv, &n_qtiles, &cl};
   const bool neg = a.scale < 0.0f;
-  const void* fn = a.causal ? (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, true> : (const void*)&fa_fwd_mxfp8_kernel<false, true>)
-                            : (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, false> : (const void*)&fa_fwd_mxfp8_kernel<false, false>);
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qtiles)), dim3(NTHREADS), args, 0, stream);
+  const void* fn = a.causal ? (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, true, NW> : (const void*)&fa_fwd_mxfp8_kernel<false, true, NW>)
+                            : (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, false, NW> : (const void*)&fa_fwd_mxfp8_kernel<false, false, NW>);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qtiles)), dim3(64 * NW), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
+}
+
+}  // namespace
+
+int launch_fa_fwd_mxfp8(const MxArgs& a, hipStream_t stream) {
+  const int64_t wg8 = a.BH * ((a.Nq + 255) / 256);
+  return wg8 >= kMx8WaveMinWorkgroups ? launch_mxfp8_nw<8>(a, stream) : launch_mxfp8_nw<4>(a, stream);
 }
 
 int launch_mx_quantize_rows(const void* X, void* E, void* S, int64_t BH, int64_t N, int64_t ldS, hipStream_t stream) {
@@ -586,7 +696,8 @@ int launch_mx_quantize_vt(const void* V, void* Vt, void* Vs, int64_t BH, int64_t
 }
 
 const char* mxfp8_config_string() {
-  return "gfx950 fa_fwd_mxfp8 v2: BR=128 (4 waves x 32 rows), BC=64, 3-stage pipeline, "
+  return "gfx950 fa_fwd_mxfp8 v3: BR=256 (8 waves x 32 rows) on grids of >= 256 such workgroups, else 128 "
+         "(4 waves), BC=64, 3-stage pipeline, plain tiles in 8 fixed MFMA segments, "
          "v_mfma_scale_f32_32x32x64_f8f6f4 for S^T=K.Q^T and O^T+=V^T.P^T, P in E4M3 (scale 1), "
          "no tile max unless a tile sum exceeds 256";
 }

@@ -169,6 +169,10 @@ MX_CASES = [
     (1, 1, 129, 65, True, 704, "one row / key past a tile"),
     (1, 2, 1, 700, False, 705, "one query"),
     (1, 1, 70, 1, False, 706, "one key"),
+    # grids of >= 256 workgroups of 256 rows: the 8-wave kernel
+    (2, 128, 300, 520, False, 720, "8 waves: ragged q tile (44 rows), ragged keys"),
+    (1, 256, 256, 1000, False, 721, "8 waves: six segmented iteration pairs, 40-key tail"),
+    (2, 128, 512, 512, True, 722, "8 waves: causal"),
 ]
 
 
@@ -201,6 +205,15 @@ def test_mxfp8_offset_keys(fa):
     o, lse = fa.fa_fwd_mxfp8(*dev, 1024, scale=SCALE)
     torch.cuda.synchronize()
     check_mx(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Qd, Kd, Vd, SCALE, False, "offset keys")
+
+
+def test_mxfp8_offset_keys_eight_waves(fa):
+    import torch
+    say("case mxfp8 on the offset-key recipe with 8-wave workgroups, B=1 H=256 Nq=256 Nk=1024")
+    dev, (Qd, Kd, Vd) = mx_case(1, 256, 256, 1024, 723, k_scale=4.0, offset_frac=0.01, offset=8.0)
+    o, lse = fa.fa_fwd_mxfp8(*dev, 1024, scale=SCALE)
+    torch.cuda.synchronize()
+    check_mx(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Qd, Kd, Vd, SCALE, False, "offset keys, 8 waves")
 
 
 def test_mxfp8_end_to_end_with_gpu_quantizers(fa):
