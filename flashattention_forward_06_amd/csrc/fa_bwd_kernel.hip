@@ -265,9 +265,37 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < NCQ; ++i) dkacc[i] = floatx16{};
 
+  // At head size 128 without a bias the LDS fragments of the S/dP and dV/dK
+  // products are read PFK MFMAs ahead of their use (a ring of PFK + 1), as in
+  // the dQ kernel.  Backward at B=2, H=16, N=8192, identical results: 650 ->
+  // 664 TFLOP/s with 2 ahead (3: 660), causal 624 -> 652 with 3 ahead (2:
+  // 637); with a per-key bias (sequential step) it lost 5 % and is not used.
+  constexpr int PFK = DQK == 128 && DV == 128 && !BIAS ? (CAUSAL ? 3 : 2) : 0;
+
   // dV^T += dO^T P and dK^T += Q^T dS, the two column-block loops interleaved
   constexpr int NCMAX = NCQ > NCV ? NCQ : NCV;
   auto dvdk = [&](const char* qs, const char* ds, int ib, const bf16x8 (&pb)[2], const bf16x8 (&dsb)[2]) FA_INLINE {
+    if constexpr (PFK > 0) {
+      // MFMA m: column block m >> 2, k half (m >> 1) & 1, dV (even m) or dK (odd m)
+      constexpr int PF = PFK, NM = 4 * NCMAX;
+      auto rd = [&](int m) FA_INLINE {
+        return (m & 1) ? tr_read_a<SWZ_BOTH, DQK>(qs, ib * 32 + ((m >> 1) & 1) * 16, m >> 2, lane)
+                       : tr_read_a<SWZ_BOTH, DV>(ds, ib * 32 + ((m >> 1) & 1) * 16, m >> 2, lane);
+      };
+      bf16x8 fr[PF + 1];
+#pragma unroll
+      for (int m = 0; m < PF; ++m) fr[m] = rd(m);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (m + PF < NM) fr[(m + PF) % (PF + 1)] = rd(m + PF);
+        const int cb = m >> 2, ks = (m >> 1) & 1;
+        if (m & 1)
+          dkacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PF + 1)], dsb[ks], dkacc[cb], 0, 0, 0);
+        else
+          dvacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PF + 1)], pb[ks], dvacc[cb], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int cb = 0; cb < NCMAX; ++cb)
 #pragma unroll
@@ -342,6 +370,24 @@ fa_bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   auto sdp = [&](const char* qs, const char* ds, int ib, floatx16& s, floatx16& dp) FA_INLINE {
     s = floatx16{};
     dp = floatx16{};
+    if constexpr (PFK > 0) {
+      constexpr int NM = NTQ + NTV;
+      auto rd = [&](int m) FA_INLINE {
+        return m < NTQ ? row_read_a<SWZ_BOTH, DQK>(qs, ib * 32, m, c, h) : row_read_a<SWZ_BOTH, DV>(ds, ib * 32, m - NTQ, c, h);
+      };
+      bf16x8 fr[PFK + 1];
+#pragma unroll
+      for (int m = 0; m < PFK; ++m) fr[m] = rd(m);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (m + PFK < NM) fr[(m + PFK) % (PFK + 1)] = rd(m + PFK);
+        if (m < NTQ)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PFK + 1)], kb[m], s, 0, 0, 0);
+        else
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PFK + 1)], vb[m - NTQ], dp, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < NTQ; ++t)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DQK>(qs, ib * 32, t, c, h), kb[t], s, 0, 0, 0);
@@ -571,9 +617,34 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // One K/V tile as two 32-key blocks, software pipelined inside the wave:
   // S/dP of block 1 are issued before the softmax of block 0, and dQ of
   // block 0 before the softmax of block 1, so the VALU work overlaps MFMAs.
+  // At head size 128 the A fragments are read PFQ MFMAs ahead of their use (a
+  // ring of PFQ + 1): one wave per SIMD has no other wave to cover the LDS
+  // latency, and the compiler's own order read each one only one or two MFMAs
+  // ahead.  Backward at B=2, H=16, N=8192, identical results: 647 -> 662
+  // TFLOP/s, causal 603 -> 634, per-key bias 508 -> 518 (2 ahead: 660, 631,
+  // 517).  At head size 64 with a bias the ring makes the kernel spill.
+  constexpr int PFQ = DQK == 128 && DV == 128 ? 3 : 0;
   auto sdp = [&](const char* ks, const char* vs, int kb, floatx16& s, floatx16& dp) FA_INLINE {
     s = floatx16{};
     dp = floatx16{};
+    if constexpr (PFQ > 0) {
+      constexpr int NM = NTQ + NTV;
+      auto rd = [&](int m) FA_INLINE {
+        return m < NTQ ? row_read_a<SWZ_BOTH, DQK>(ks, kb * 32, m, c, h) : row_read_a<SWZ_ROW, DV>(vs, kb * 32, m - NTQ, c, h);
+      };
+      bf16x8 fr[PFQ + 1];
+#pragma unroll
+      for (int m = 0; m < PFQ; ++m) fr[m] = rd(m);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (m + PFQ < NM) fr[(m + PFQ) % (PFQ + 1)] = rd(m + PFQ);
+        if (m < NTQ)
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PFQ + 1)], qb[m], s, 0, 0, 0);
+        else
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PFQ + 1)], dob[m - NTQ], dp, 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < NTQ; ++t)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_read_a<SWZ_BOTH, DQK>(ks, kb * 32, t, c, h), qb[t], s, 0, 0, 0);
@@ -599,6 +670,20 @@ fa_bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     }
   };
   auto dq_acc = [&](const char* ks, int kb, const bf16x8 (&dsb)[2]) FA_INLINE {
+    if constexpr (PFQ > 0) {
+      constexpr int NM = 2 * (CB1 - CB0);
+      auto rd = [&](int m) FA_INLINE { return tr_read_a<SWZ_BOTH, DQK>(ks, kb * 32 + (m & 1) * 16, CB0 + (m >> 1), lane); };
+      bf16x8 fr[PFQ + 1];
+#pragma unroll
+      for (int m = 0; m < PFQ && m < NM; ++m) fr[m] = rd(m);
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        if (m + PFQ < NM) fr[(m + PFQ) % (PFQ + 1)] = rd(m + PFQ);
+        const int cb = CB0 + (m >> 1);
+        dqacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (PFQ + 1)], dsb[m & 1], dqacc[cb], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int cb = CB0; cb < CB1; ++cb)
 #pragma unroll
@@ -830,9 +915,10 @@ int launch_fa_bwd(const BwdArgs& a, hipStream_t stream) {
 }
 
 const char* bwd_config_string() {
-  return "gfx950 fa_bwd v6: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
+  return "gfx950 fa_bwd v7: delta kernel; dK/dV kernel (128 keys per workgroup, 32 per wave, query blocks of 64, "
          "K and V in registers); dQ kernel (128 rows per workgroup, 64-key tiles); in-wave MFMA/VALU interleave "
          "(causal at d=128 too); two tiles per loop trip at d=128 for the causal dK/dV and the bias dQ kernels; "
+         "LDS fragments read 2-3 MFMAs ahead at d=128; "
          "two waves per SIMD at head size 64; at head size 256 one dK/dV launch per gradient "
          "and one dQ launch per column half (bias too); "
          "head sizes 64, 128, 192/128, 256; "
