@@ -133,7 +133,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // grid of one workgroup per CU (B=1, H=8, Nq=4096, Nk=8192), identical
   // results.  With the causal mask it gained there too (+5 %) but lost 1 % on
   // the 16K-token workload, so the causal kernels keep the plain iteration.
-  constexpr bool SEG_ITER = DQK == 128 && DV == 128 && BC == 64 && !CAUSAL && !BIAS;
+  // At head size 64 (16 MFMAs per tile, two scores per segment): +2 % at
+  // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.
+  constexpr bool SEG_ITER = ((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !CAUSAL && !BIAS && !SPLIT),
                 "8-wave workgroups are built for the plain head-size-128 kernel only");
   constexpr int BR = 32 * NW;                 // query rows per workgroup
@@ -694,17 +696,24 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     tile_to_lds<BC, SWZ_TR, DV, NW>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
     const char* ks = kbuf(P);
     const char* vs = vbuf(P);
-    // MFMA m < 16: S block m & 1, k step m >> 1; MFMA 16 + m: output block
-    // m & 3, keys 16 (m >> 2) .. +15
+    // NS MFMAs of S (m < NS: key block m % KB, k step m / KB), then NP of
+    // P V (NS + m: output block m % NCB, keys 16 (m / NCB) .. +15); SPS of
+    // the lane's 32 scores per segment
+    constexpr int NS = KB * NT, NP = NCB * (BC / 16), NM = NS + NP, SPS = 32 / NM;
+    static_assert(KB == 2 && SPS * NM == 32 && (SPS == 1 || SPS % 2 == 0), "segment layout");
+    constexpr int CSH = NCB == 4 ? 2 : 1;  // log2(NCB)
+    static_assert(NCB == (1 << CSH), "output blocks");
     auto kfrag = [&](int m) FA_INLINE {
       return __builtin_bit_cast(bf16x8,
                                 *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>((m & 1) * 32 + c, 2 * (m >> 1) + h)));
     };
-    auto vfrag = [&](int m) FA_INLINE { return tr_read_a<SWZ_TR, DV>(vs, (uint32_t)((m >> 2) * 16), m & 3, lane); };
-    floatx16 s2[2];
+    auto vfrag = [&](int m) FA_INLINE {
+      return tr_read_a<SWZ_TR, DV>(vs, (uint32_t)((m >> CSH) * 16), m & (NCB - 1), lane);
+    };
+    floatx16 s2[KB];
     s2[0] = floatx16{};
     s2[1] = floatx16{};
-    bf16x8 kf[PF + 1], vf[PF + 1], pn[4];
+    bf16x8 kf[PF + 1], vf[PF + 1], pn[2 * KB];
     float pe[32];
     float lsum = 0.0f, lrnd = 0.0f;
     const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
@@ -725,24 +734,33 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int r = 0; r < AHEAD; ++r) score(r);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < NM; ++i) {
       const int nxt = i + PF;  // the MFMA whose operand is read in this segment
-      if (nxt < 16) kf[nxt % (PF + 1)] = kfrag(nxt);
-      else if (nxt < 32) vf[(nxt - 16) % (PF + 1)] = vfrag(nxt - 16);
-      if (i + AHEAD < 32) score(i + AHEAD);
-      if (i & 1) pack(i >> 1);
-      if (i < 16) {
+      if (nxt < NS) kf[nxt % (PF + 1)] = kfrag(nxt);
+      else if (nxt < NM) vf[(nxt - NS) % (PF + 1)] = vfrag(nxt - NS);
+      if constexpr (SPS == 1) {
+        if (i + AHEAD < 32) score(i + AHEAD);
+        if (i & 1) pack(i >> 1);
+      } else {
+#pragma unroll
+        for (int u = 0; u < SPS; ++u)
+          if (SPS * i + u + AHEAD < 32) score(SPS * i + u + AHEAD);
+#pragma unroll
+        for (int u = 0; u < SPS / 2; ++u) pack(i * (SPS / 2) + u);
+      }
+      if (i < NS) {
         s2[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qb[i >> 1], s2[i & 1], 0, 0, 0);
       } else {
-        const int m = i - 16;
-        oacc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m % (PF + 1)], pb[m >> 2], oacc[m & 3], 0, 0, 0);
+        const int m = i - NS;
+        oacc[m & (NCB - 1)] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m % (PF + 1)], pb[m >> CSH], oacc[m & (NCB - 1)], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // a lane's tile sum above 2^16 (or not finite): recompute with the max
     const bool fix = __ballot(!(lsum <= 65536.0f)) != 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) keep(pn[i]);
+    for (int i = 0; i < 2 * KB; ++i) keep(pn[i]);
     keep(lsum);
     keep(lrnd);
     float alpha = 1.0f;
@@ -755,7 +773,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     keep(l_run);
     keep(l_rnd);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pb[i] = pn[i];
+    for (int i = 0; i < 2 * KB; ++i) pb[i] = pn[i];
     s1[0] = s2[0];
     s1[1] = s2[1];
     wait_vmem();
@@ -997,9 +1015,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v8: BR=128 (4 waves x 32 rows; 256 = 8 waves for plain head size 128 on grids of >= 256 "
-         "workgroups), plain head-size-128 tiles without mask or bias in 32 fixed MFMA segments, BC=64 (32 with "
-         "bias), 3-stage K/V pipeline "
+  return "gfx950 fa_fwd v9: BR=128 (4 waves x 32 rows; 256 = 8 waves for plain head size 128 on grids of >= 256 "
+         "workgroups), plain tiles without mask or bias in fixed MFMA segments (32 at head size 128, 16 at 64), "
+         "BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
          "per SIMD at head size 64 with a bias), "
