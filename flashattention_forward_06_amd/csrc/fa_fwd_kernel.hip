@@ -126,7 +126,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
               float* __restrict__ Lpart, int split_keys, int n_splits) {
   // SEG: 8 waves share each K/V tile (SEG_ITER below: plain tiles run the
   // segmented iteration, iteration_seg: one MFMA per segment, the 16 of
-  // S(j+2), then the 16 of P(j) V(j)... see there).
+  // S(j+2), then the 16 of P(j) V(j)... see there; with the causal mask the
+  // tiles on the diagonal keep the masked iteration).
   constexpr bool SEG = NW == 8;
   // The segmented iteration also runs the plain tiles of the 4-wave head-size-
   // 128 kernels without mask or bias (including the key split): +6.5 % on a
@@ -135,9 +136,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // the 16K-token workload, so the causal kernels keep the plain iteration.
   // At head size 64 (16 MFMAs per tile, two scores per segment): +2 % at
   // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.
-  constexpr bool SEG_ITER = ((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS;
-  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !CAUSAL && !BIAS && !SPLIT),
-                "8-wave workgroups are built for the plain head-size-128 kernel only");
+  constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
+  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !SPLIT),
+                "8-wave workgroups are built for the head-size-128 kernels without bias or key split only");
   constexpr int BR = 32 * NW;                 // query rows per workgroup
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
   constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
@@ -908,11 +909,16 @@ const void* kernel_ptr() {
 }
 
 // Grids of the 8-wave kernel: at least one 256-row workgroup per CU (MI355X
-// has 256); smaller launches keep 128-row workgroups, two per CU.
+// has 256); smaller launches keep 128-row workgroups, two per CU.  With the
+// causal mask also at least 8192 query rows: each 256-row workgroup then
+// masks 5 key tiles on its diagonal instead of 3, which the shorter
+// sequences do not repay (causal, in one process: N = 8192 +1.4 %, 16384
+// +2.0 %, 4096 -3.1 %).
 constexpr int64_t kSegMinWorkgroups = 256;
+constexpr int64_t kSegCausalMinRows = 8192;
 bool use_seg(const LaunchArgs& a) {
-  return a.d == 128 && a.dv == 128 && !a.causal && a.bias == nullptr && a.n_splits <= 1 &&
-         a.BH * ((a.Nq + 255) / 256) >= kSegMinWorkgroups;
+  return a.d == 128 && a.dv == 128 && (!a.causal || a.Nq >= kSegCausalMinRows) && a.bias == nullptr &&
+         a.n_splits <= 1 && a.BH * ((a.Nq + 255) / 256) >= kSegMinWorkgroups;
 }
 
 // Kernel for one pair of head sizes: BC = 64 keys per tile (32 at head size
@@ -992,8 +998,10 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                   &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = seg   ? (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8>()
-                                 : kernel_ptr<128, 128, 64, false, false, false, false, 8>())
+  const void* fn = seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()
+                                            : kernel_ptr<128, 128, 64, false, true, false, false, 8>())
+                                     : (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8>()
+                                            : kernel_ptr<128, 128, 64, false, false, false, false, 8>()))
                    : split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
                            : select_pair<false>(a.d, a.dv, neg, a.causal, b);
   if (fn == nullptr) return (int)hipErrorInvalidValue;
@@ -1015,9 +1023,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v9: BR=128 (4 waves x 32 rows; 256 = 8 waves for plain head size 128 on grids of >= 256 "
-         "workgroups), plain tiles without mask or bias in fixed MFMA segments (32 at head size 128, 16 at 64), "
-         "BC=64 (32 with bias), 3-stage K/V pipeline "
+  return "gfx950 fa_fwd v10: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
+         ">= 256 workgroups, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA segments (32 at "
+         "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
          "per SIMD at head size 64 with a bias), "

@@ -5,6 +5,7 @@ configuration the benchmark times) are compared element by element over the
 whole output.
 """
 import math
+import time
 
 import numpy as np
 import pytest
@@ -227,6 +228,46 @@ def test_causal_offset_keys_sampled(fa):
     idx = torch.from_numpy(rows).cuda()
     check_parity(o.view(-1, 128)[idx].float().cpu().numpy().astype(np.float64),
                  lse.view(-1)[idx].cpu().numpy().astype(np.float64), Or, Lr, "causal koffset (sampled)")
+
+
+# Causal launches of at least 8192 query rows on grids of >= 256 workgroups
+# of 256 rows run the 8-wave kernel (segmented plain tiles, masked diagonal).
+EIGHT_WAVE_CAUSAL_CASES = [
+    # B, H, Nq, Nk, seed, note
+    (1, 8, 8192, 8192, 90, "square: 32 diagonal tiles of 256 rows per head"),
+    (1, 8, 8492, 8000, 91, "Nq > Nk: 492 leading rows see no key, ragged q tile and kv tail"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,note", EIGHT_WAVE_CAUSAL_CASES)
+def test_causal_eight_wave_full_compare(fa, B, H, Nq, Nk, seed, note):
+    import torch
+    say(f"case causal 8-wave B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(128), causal=True)
+    torch.cuda.synchronize()
+    Og, Lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    t0 = time.time()
+    Oo, Lo = oracle.attention_masked(Q, K, V, 1 / math.sqrt(128), causal=True)
+    say(f"  oracle: {B * H * Nq} rows in {time.time() - t0:.1f} s")
+    none = np.isneginf(Lo)
+    assert np.array_equal(np.isneginf(Lg), none), "rows that see no key must report LSE = -inf"
+    assert np.all(Og[none] == 0)
+    check_parity(Og[~none], Lg[~none], Oo[~none], Lo[~none], f"causal 8-wave {note}")
+
+
+def test_causal_eight_wave_offset_keys_sampled(fa):
+    import torch
+    w = fi.WORKLOADS["b1_h16_n16384_koffset"]
+    say("case causal 8-wave on the 16K offset-key workload (sampled rows)")
+    Q, K, V = fi.make_workload(w)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    rows = fi.sample_rows(w.B, w.H, w.Nq, 256, seed=w.seed)
+    Or, Lr = oracle.attention_masked(Q, K, V, w.scale, causal=True, rows=rows)
+    idx = torch.from_numpy(rows).cuda()
+    check_parity(o.view(-1, 128)[idx].float().cpu().numpy().astype(np.float64),
+                 lse.view(-1)[idx].cpu().numpy().astype(np.float64), Or, Lr, "causal 8-wave koffset (sampled)")
 
 
 def test_noncausal_unchanged_by_masked_entry(fa):
