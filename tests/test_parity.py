@@ -256,6 +256,17 @@ def test_causal_eight_wave_full_compare(fa, B, H, Nq, Nk, seed, note):
     check_parity(Og[~none], Lg[~none], Oo[~none], Lo[~none], f"causal 8-wave {note}")
 
 
+@pytest.mark.parametrize("scale,note", [(-1 / math.sqrt(128), "negative scale"), (0.0, "zero scale")])
+def test_causal_eight_wave_scales(fa, scale, note):
+    import torch
+    say(f"case causal 8-wave B=1 H=8 N=8192 scale={scale} ({note})")
+    Q, K, V = fi.make_qkv(1, 8, 8192, 8192, 128, seed=92)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=scale, causal=True)
+    torch.cuda.synchronize()
+    Oo, Lo = oracle.attention_masked(Q, K, V, scale, causal=True)
+    check_parity(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Oo, Lo, f"causal 8-wave {note}")
+
+
 def test_causal_eight_wave_offset_keys_sampled(fa):
     import torch
     w = fi.WORKLOADS["b1_h16_n16384_koffset"]

@@ -198,6 +198,18 @@ def test_mxfp8_scale_variants(fa, scale, note):
                  f"{note} causal={causal}")
 
 
+@pytest.mark.parametrize("scale,note", [(-0.09, "negative scale"), (0.0, "zero scale")])
+def test_mxfp8_eight_wave_scales(fa, scale, note):
+    import torch
+    say(f"case mxfp8 8-wave B=1 H=256 Nq=256 Nk=520 scale={scale} ({note})")
+    dev, (Qd, Kd, Vd) = mx_case(1, 256, 256, 520, 724)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd_mxfp8(*dev, 520, scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        check_mx(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Qd, Kd, Vd, scale, causal,
+                 f"8-wave {note} causal={causal}")
+
+
 def test_mxfp8_offset_keys(fa):
     import torch
     say("case mxfp8 on the offset-key recipe, B=1 H=2 N=1024")
