@@ -535,20 +535,26 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     return alpha;
   };
 
-  // The same for unmasked tiles with a bias: the logits t = s*c + b*log2(e)
-  // are written over the scores, P = exp2(t - m_run).  A row that has seen
-  // only -inf logits so far gives NaN (-inf - -inf), which also sends the
-  // tile to the slow path (softmax_fix_logits), where such rows keep P = 0.
-  auto softmax_fast_bias = [&](floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB],
+  // The same for unmasked tiles with a bias.  At head size 64, P =
+  // exp2(s*c + (b*log2(e) - m_run)) as two FMAs (+4 % with a per-key bias);
+  // elsewhere the logits t = s*c + b*log2(e) and then exp2(t - m_run), the
+  // form that measured faster there.  A row that has seen only -inf logits so
+  // far (m_run = -inf) gives +inf or NaN, which sends the tile to the slow
+  // path (softmax_fix_logits): it forms the logits and takes their max, and
+  // rows that see only -inf keep P = 0 there.
+  auto softmax_fast_bias = [&](const floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB],
                                float& lsum_out, float& lrnd_out) FA_INLINE -> bool {
     float lsum = 0.0f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float t = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
-        s[kb][r] = t;
-        const float p = __builtin_amdgcn_exp2f(t - m_run);
+        float p;
+        if constexpr (DQK == 64)
+          p = __builtin_amdgcn_exp2f(
+              __builtin_fmaf(s[kb][r], c_log2, __builtin_fmaf(bt[kb][r >> 2][r & 3], LOG2E, -m_run)));
+        else
+          p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E) - m_run);
         lsum += p;
         pb[kb * 2 + (r >> 3)][r & 7] = (__bf16)p;
       }
@@ -556,8 +562,13 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     lrnd_out = rounded_sum(pb);
     return __ballot(!(lsum <= 65536.0f)) != 0;
   };
-  auto softmax_fix_logits = [&](const floatx16 (&t)[KB], bf16x8 (&pb)[2 * KB], float& lsum_out,
-                                float& lrnd_out) FA_INLINE -> float {
+  auto softmax_fix_logits = [&](const floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB],
+                                float& lsum_out, float& lrnd_out) FA_INLINE -> float {
+    floatx16 t[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t[kb][r] = __builtin_fmaf(s[kb][r], c_log2, bt[kb][r >> 2][r & 3] * LOG2E);
     float ext = t[0][0];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -651,7 +662,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         keep(lsum_f);
         keep(lrnd_f);
         if (fix) {
-          if constexpr (BIAS) alpha = softmax_fix_logits(s1, pn, lsum_f, lrnd_f);
+          if constexpr (BIAS) alpha = softmax_fix_logits(s1, bcur, pn, lsum_f, lrnd_f);
           else alpha = softmax_fix(s1, pn, lsum_f, lrnd_f);
           rs = true;
         }
@@ -1023,12 +1034,12 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v10: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
+  return "gfx950 fa_fwd v11: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
          ">= 256 workgroups, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
-         "per SIMD at head size 64 with a bias), "
+         "per SIMD and a two-FMA exponent at head size 64 with a bias), "
          "V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; "
          "fp32 additive bias; key split with LSE merge";
 }
