@@ -45,12 +45,12 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # reads for a plain copy kernel of known size (read x2.000, write x1.000).
 # Reported only while the library's build string is the one measured; any
 # other kernel build reports null.  (The string last changed for the 4-wave
-# kernels at head sizes 64 and 128, the causal kernel and the head-size-64
-# bias kernel; the 8-wave kernel that the default workload runs compiles to
-# the same machine code as when it was measured.)
+# kernels at head sizes 64 and 128, the causal kernel, the head-size-64
+# bias kernel and the key split; the 8-wave kernel that the default workload
+# runs compiles to the same machine code as when it was measured.)
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v11: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids "
-              "of >= 256 workgroups, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA "
+    "kernel": "gfx950 fa_fwd v12: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids "
+              "of >= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA "
               "segments (32 at head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline (S two tiles "
               "ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 (K fragments "
               "read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves per "

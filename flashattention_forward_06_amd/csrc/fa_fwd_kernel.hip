@@ -137,8 +137,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // At head size 64 (16 MFMAs per tile, two scores per segment): +2 % at
   // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.
   constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
-  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !SPLIT),
-                "8-wave workgroups are built for the head-size-128 kernels without bias or key split only");
+  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)),
+                "8-wave workgroups are built for the head-size-128 kernels without bias (key split: no mask)");
   constexpr int BR = 32 * NW;                 // query rows per workgroup
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
   constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
@@ -924,12 +924,15 @@ const void* kernel_ptr() {
 // causal mask also at least 8192 query rows: each 256-row workgroup then
 // masks 5 key tiles on its diagonal instead of 3, which the shorter
 // sequences do not repay (causal, in one process: N = 8192 +1.4 %, 16384
-// +2.0 %, 4096 -3.1 %).
+// +2.0 %, 4096 -3.1 %).  A key split without the mask counts its
+// ranges: B=1, H=8, Nq=4096, Nk=8192 in two ranges is 256 such workgroups.
 constexpr int64_t kSegMinWorkgroups = 256;
 constexpr int64_t kSegCausalMinRows = 8192;
 bool use_seg(const LaunchArgs& a) {
-  return a.d == 128 && a.dv == 128 && (!a.causal || a.Nq >= kSegCausalMinRows) && a.bias == nullptr &&
-         a.n_splits <= 1 && a.BH * ((a.Nq + 255) / 256) >= kSegMinWorkgroups;
+  const int64_t ranges = a.n_splits > 1 ? a.n_splits : 1;
+  if (a.d != 128 || a.dv != 128 || a.bias != nullptr) return false;
+  if (a.causal && (ranges > 1 || a.Nq < kSegCausalMinRows)) return false;
+  return a.BH * ((a.Nq + 255) / 256) * ranges >= kSegMinWorkgroups;
 }
 
 // Kernel for one pair of head sizes: BC = 64 keys per tile (32 at head size
@@ -1009,10 +1012,12 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                   &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()
-                                            : kernel_ptr<128, 128, 64, false, true, false, false, 8>())
-                                     : (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8>()
-                                            : kernel_ptr<128, 128, 64, false, false, false, false, 8>()))
+  const void* fn = seg && split ? (neg ? kernel_ptr<128, 128, 64, true, false, false, true, 8>()
+                                       : kernel_ptr<128, 128, 64, false, false, false, true, 8>())
+                   : seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()
+                                              : kernel_ptr<128, 128, 64, false, true, false, false, 8>())
+                                       : (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8>()
+                                              : kernel_ptr<128, 128, 64, false, false, false, false, 8>()))
                    : split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
                            : select_pair<false>(a.d, a.dv, neg, a.causal, b);
   if (fn == nullptr) return (int)hipErrorInvalidValue;
@@ -1034,8 +1039,8 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v11: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
-         ">= 256 workgroups, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA segments (32 at "
+  return "gfx950 fa_fwd v12: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
+         ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "

@@ -62,6 +62,28 @@ def test_split_full_compare(fa, d, dv, B, H, Nq, Nk, causal, n, seed, note):
     compare(fa, Q, K, V, 1.0 / math.sqrt(d), causal, n, note)
 
 
+# Key splits whose grid holds at least 256 workgroups of 256 query rows
+# (B*H*ceil(Nq/256)*ranges >= 256, no mask, no bias): the ranges run the
+# 8-wave head-size-128 kernel with the segmented iteration.
+SEG_SPLIT_CASES = [
+    # B, H, Nq, Nk, n_splits, seed, scale, kwargs, note
+    (1, 8, 4096, 8192, 0, 520, None, {}, "the 5090 benchmark shape, automatic plan (two ranges)"),
+    (1, 128, 300, 129, 2, 521, None, {}, "ranges of 128 keys and of 1 key, ragged q tile"),
+    (2, 64, 256, 1000, 3, 522, None, {}, "three ranges, ragged last"),
+    (1, 128, 256, 2000, 4, 523, -0.07, dict(k_scale=4.0, offset_frac=0.01, offset=8.0),
+     "negative scale, large logits (the 16K workload's recipe)"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,n,seed,scale,kw,note", SEG_SPLIT_CASES)
+def test_split_eight_wave_full_compare(fa, B, H, Nq, Nk, n, seed, scale, kw, note):
+    used = fa.splitkv_workspace_bytes(B, H, Nq, Nk, 128, n)[1]
+    assert B * H * ((Nq + 255) // 256) * used >= 256
+    say(f"case split 8-wave B={B} H={H} Nq={Nq} Nk={Nk} n={n} -> {used} ranges ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed, **kw)
+    compare(fa, Q, K, V, 1.0 / math.sqrt(128) if scale is None else scale, False, n, note)
+
+
 def test_split_bias_negative_scale_and_offsets(fa):
     say("case split: bias with -inf keys (causal and not), negative scale, offset-key recipe")
     Q, K, V = fi.make_qkv(1, 2, 190, 1100, 128, seed=510, k_scale=4.0, offset_frac=0.02, offset=8.0)
