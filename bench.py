@@ -49,8 +49,9 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # bias kernel and the key split; the 8-wave kernel that the default workload
 # runs compiles to the same machine code as when it was measured.)
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v12: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids "
-              "of >= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA "
+    "kernel": "gfx950 fa_fwd v13: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids "
+              "of >= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key "
+              "groups of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA "
               "segments (32 at head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline (S two tiles "
               "ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 (K fragments "
               "read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves per "

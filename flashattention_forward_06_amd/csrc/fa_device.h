@@ -97,6 +97,20 @@ __device__ inline void tile_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t row0, char
   const uint32_t soff = __builtin_amdgcn_readfirstlane(row0 * RB);
   static_assert(ROWS * (int)RB % (1024 * NW) == 0, "tile must be whole 1 KiB blocks per wave");
   constexpr int N_INST = ROWS * (int)RB / 1024 / NW;
+  if constexpr ((RB & (RB - 1)) == 0 && (NW * 1024 / (int)RB) % 16 == 0) {
+    // Instruction i covers the rows of instruction 0 plus i*NW*1024/RB, a
+    // multiple of 16 rows, so every swizzle maps them alike: one vector
+    // offset, and the step in the scalar offset.
+    const uint32_t row = (uint32_t)wave * (1024u / RB) + (uint32_t)lane / (RB / 16u);
+    const uint32_t pos = (uint32_t)lane & (RB / 16u - 1u);
+    const uint32_t voff = row * RB + (swz_chunk<S, DIM>(row, pos) << 4);
+#pragma unroll
+    for (int i = 0; i < N_INST; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)((lds_char*)lds + (uint32_t)(i * NW + wave) * 1024u), 16, voff,
+          soff + (uint32_t)(i * NW) * 1024u, 0, 0);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < N_INST; ++i) {
     const uint32_t blk = (uint32_t)(i * NW + wave);          // which 1 KiB block

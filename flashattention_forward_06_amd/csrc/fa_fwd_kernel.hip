@@ -116,7 +116,11 @@ constexpr float RESCALE_SLACK = 8.0f;        // log2 units: P stays <= 256
 //             [n_splits, B*H, Nq]; a merge kernel combines the ranges
 //   NW        waves per workgroup: 4, or 8 for the plain head-size-128 kernel
 //             (SEG below), whose workgroups cover 256 query rows
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4>
+//   KS2       (8 waves only) two groups of 4 waves attend to the two halves
+//             of the key tiles for the same 128 query rows and combine their
+//             results through LDS at the end: the key split inside one
+//             workgroup, for launches with one 128-row workgroup per CU
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4, bool KS2 = false>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd(DQK, DV, BIAS), waves_per_simd(DQK, DV, BIAS))))
 fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -139,7 +143,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)),
                 "8-wave workgroups are built for the head-size-128 kernels without bias (key split: no mask)");
-  constexpr int BR = 32 * NW;                 // query rows per workgroup
+  static_assert(!KS2 || (NW == 8 && !CAUSAL && !SPLIT), "the in-workgroup key split: 8 waves, no mask, no split");
+  constexpr int NWR = KS2 ? NW / 2 : NW;      // waves per key group (all waves without KS2)
+  constexpr int BR = 32 * NWR;                // query rows per workgroup
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
   constexpr int RBQ = 2 * DQK;                // bytes per Q or K row
   constexpr int RBV = 2 * DV;                 // bytes per V or O row
@@ -154,6 +160,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   const int lane = tid & 63;
   const int c = lane & 31;   // query column of the S^T / O^T accumulators
   const int h = lane >> 5;   // half of the wave
+  const int wr = KS2 ? (wave & (NWR - 1)) : wave;  // which 32 rows of the workgroup
+  const int kg_u = KS2 ? __builtin_amdgcn_readfirstlane(wave / NWR) : 0;  // key group (KS2)
 
   // XCD-aware remap: consecutive logical tiles (same head) go to one XCD.
   const int nblk = gridDim.x;
@@ -186,8 +194,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
   // this workgroup's keys: [k0, k0 + Nk) of the head's Nk_all
-  const int k0 = SPLIT ? split * split_keys : 0;
-  const int Nk = SPLIT ? (Nk_all - k0 < split_keys ? Nk_all - k0 : split_keys) : Nk_all;
+  // KS2: group g takes key tiles [g*G, (g+1)*G) of the head's ceil(Nk/BC),
+  // G = half of them rounded up; both groups run G iterations (the second
+  // group's last one may lie past Nk: fully masked, all weights 0), so every
+  // barrier is reached by all waves
+  const int ks_tiles = KS2 ? ((Nk_all + BC - 1) / BC + 1) / 2 : 0;
+  const int k0 = SPLIT ? split * split_keys : (KS2 ? kg_u * ks_tiles * BC : 0);
+  int Nk = SPLIT ? (Nk_all - k0 < split_keys ? Nk_all - k0 : split_keys) : Nk_all;
+  if constexpr (KS2) Nk = Nk_all - k0 <= 0 ? 0 : (Nk_all - k0 < ks_tiles * BC ? Nk_all - k0 : ks_tiles * BC);
   // output rows: the head's O / LSE, or this range's slice of the partials
   const int BH = SPLIT ? nblk / (n_splits * n_qtiles) : 0;
   const size_t orow0 = SPLIT ? ((size_t)split * (size_t)BH + (size_t)bh) * (size_t)Nq : (size_t)bh * (size_t)Nq;
@@ -202,8 +216,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float* const lse_out = SPLIT ? Lpart : LSE;
 
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wr_u = __builtin_amdgcn_readfirstlane(wr);
   const int n_full = Nk / BC;  // tiles with BC valid keys
-  int n_tiles = n_full + (Nk % BC != 0);
+  int n_tiles = KS2 ? ks_tiles : n_full + (Nk % BC != 0);
   int first_masked = n_full;   // first tile that needs per-key masks
   // last key visible to this lane's query row (keys above it are masked)
   int key_lim = Nk - 1;
@@ -216,11 +231,11 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     n_tiles = need < n_tiles ? need : n_tiles;
     const int unmasked = lim_first + 1 <= 0 ? 0 : (lim_first + 1) / BC;
     first_masked = unmasked < first_masked ? unmasked : first_masked;
-    const int my_lim = q0 + wave * 32 + c + off;
+    const int my_lim = q0 + wr * 32 + c + off;
     key_lim = my_lim < key_lim ? my_lim : key_lim;
     if (n_tiles == 0) {
       // no row of this q-tile sees any key: O = 0, LSE = -inf
-      const int q = q0 + wave * 32 + c;
+      const int q = q0 + wr * 32 + c;
       constexpr uint32_t ORB = SPLIT ? 4 * DV : RBV;  // bytes per output row
 #pragma unroll
       for (int i = 0; i < (int)ORB / 32; ++i)  // this lane's half row: bytes [ORB/2*h, ORB/2*(h+1))
@@ -243,7 +258,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int hd = bh - b * H;
     // wave_u, not wave: the resource must be provably wave-uniform, or the
     // compiler wraps every load in a loop over the distinct descriptors
-    const int qw0 = q0 + wave_u * 32;
+    const int qw0 = q0 + wr_u * 32;
     const int nrows = Nq - qw0 < 32 ? Nq - qw0 : 32;
     const float* base = bias + (int64_t)b * bias_sb + (int64_t)hd * bias_sh + (int64_t)qw0 * bias_sq + k0;
     const uint32_t bytes = nrows > 0 ? (uint32_t)(((int64_t)(nrows - 1) * bias_sq + Nk) * 4) : 0u;
@@ -266,22 +281,37 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // With SEG each buffer is its own LDS array: every loop body reads one
   // buffer while the LDS-direct copies fill another, and as distinct objects
   // the compiler can tell that the reads need not wait for those copies.
-  __shared__ __attribute__((aligned(1024))) char seg_k0[SEG ? K_TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char seg_k1[SEG ? K_TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char seg_v0[SEG ? V_TILE : 16];
-  __shared__ __attribute__((aligned(1024))) char seg_v1[SEG ? V_TILE : 16];
+  // (KS2: one K_TILE / V_TILE per key group in each array)
+  constexpr int NKG = KS2 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char seg_k0[SEG ? NKG * K_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_k1[SEG ? NKG * K_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_v0[SEG ? NKG * V_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char seg_v1[SEG ? NKG * V_TILE : 16];
   auto kbuf = [&](int i) FA_INLINE -> char* {
-    if constexpr (SEG) return i ? seg_k1 : seg_k0;
+    if constexpr (KS2) return (i ? seg_k1 : seg_k0) + kg_u * K_TILE;
+    else if constexpr (SEG) return i ? seg_k1 : seg_k0;
     else return smem + i * K_TILE;
   };
   auto vbuf = [&](int i) FA_INLINE -> char* {
-    if constexpr (SEG) return i ? seg_v1 : seg_v0;
+    if constexpr (KS2) return (i ? seg_v1 : seg_v0) + kg_u * V_TILE;
+    else if constexpr (SEG) return i ? seg_v1 : seg_v0;
     else return smem + 2 * K_TILE + i * V_TILE;
   };
 
   // ---- prologue: the Q tile through LDS into registers.
   bf16x8 qb[NT];  // qb[t]: Q[q0 + wave*32 + c][16t + 8h .. +7]
-  if constexpr (SEG) {
+  if constexpr (KS2) {
+    // 128 rows in two 64-row pieces (the first K buffers), read by both groups
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0, seg_k0, wave_u, lane);
+    tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0 + 64, seg_k1, wave_u, lane);
+    wait_vmem();
+    __syncthreads();
+    const char* qs = (wr_u >> 1) == 0 ? seg_k0 : seg_k1;
+    const uint32_t row = (wr_u & 1) * 32 + c;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(qs + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
+  } else if constexpr (SEG) {
     // 256 rows in four 64-row pieces, one per K/V buffer
     tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0, kbuf(0), wave_u, lane);
     tile_to_lds<64, SWZ_ROW, DQK, NW>(rq, q0 + 64, kbuf(1), wave_u, lane);
@@ -305,9 +335,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       qb[t] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uintx4*>(smem + swz<SWZ_ROW, DQK>(row, 2 * t + h)));
   }
   __syncthreads();  // the Q staging area is reused from here on
-  tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, 0, kbuf(0), wave_u, lane);
-  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, BC, kbuf(1), wave_u, lane);
-  tile_to_lds<BC, SWZ_TR, DV, NW>(rv, 0, vbuf(0), wave_u, lane);
+  tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, 0, kbuf(0), wr_u, lane);
+  if (n_tiles > 1) tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, BC, kbuf(1), wr_u, lane);
+  tile_to_lds<BC, SWZ_TR, DV, NWR>(rv, 0, vbuf(0), wr_u, lane);
   floatx4 b0[KB][4], bcur[KB][4];  // bias of tile 0 / of the tile whose softmax is next
   if constexpr (BIAS) {
     load_bias(0, b0);
@@ -393,7 +423,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   auto softmax = [&](floatx16 (&s)[KB], const floatx4 (&bt)[KB][4], bf16x8 (&pb)[2 * KB], int lim,
                      auto mask_tag, bool& rescale) FA_INLINE -> float {
     constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;  // a row may see no key (yet)
+    constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS || KS2;  // a row may see no key (yet)
     // LOGIT: the tile's scores are first turned into log2-domain logits t
     // (bias added, hidden keys set to -inf), so the max and the exponent use
     // t directly and a hidden key gives exp2(-inf) = 0 whatever the scale
@@ -615,7 +645,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if (n_tiles > 1) scores(kbuf(1), s1);
   }
   __syncthreads();  // K(0) consumed: K(2) goes into its buffer
-  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, 2 * BC, kbuf(0), wave_u, lane);
+  if (n_tiles > 2) tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, 2 * BC, kbuf(0), wr_u, lane);
   wait_vmem();
   __syncthreads();
 
@@ -633,8 +663,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int P = decltype(par_tag)::value;  // == j & 1
     constexpr bool HAS_S2 = decltype(has_s2_tag)::value;
     constexpr bool HAS_S1 = decltype(has_s1_tag)::value;
-    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DV, NW>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, (j + 3) * BC, kbuf(P ^ 1), wr_u, lane);
+    if constexpr (HAS_S1) tile_to_lds<BC, SWZ_TR, DV, NWR>(rv, (j + 1) * BC, vbuf(P ^ 1), wr_u, lane);
     if constexpr (BIAS && HAS_S2) load_bias(j + 2, bnext);
     floatx16 s2[KB];
     if constexpr (HAS_S2) scores(kbuf(P), s2);
@@ -704,8 +734,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     if constexpr (SEG_ITER) {
     constexpr int P = decltype(par_tag)::value;
     constexpr int PF = 3, AHEAD = 2;
-    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NW>(rk, (j + 3) * BC, kbuf(P ^ 1), wave_u, lane);
-    tile_to_lds<BC, SWZ_TR, DV, NW>(rv, (j + 1) * BC, vbuf(P ^ 1), wave_u, lane);
+    if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, (j + 3) * BC, kbuf(P ^ 1), wr_u, lane);
+    tile_to_lds<BC, SWZ_TR, DV, NWR>(rv, (j + 1) * BC, vbuf(P ^ 1), wr_u, lane);
     const char* ks = kbuf(P);
     const char* vs = vbuf(P);
     // NS MFMAs of S (m < NS: key block m % KB, k step m / KB), then NP of
@@ -823,7 +853,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   int j_split = first_masked - 1;
   j_split = j_split < 0 ? 0 : (j_split > j_end ? j_end : j_split);
   run(0, j_split, F{});
-  if constexpr (CAUSAL) run(j_split, j_end, T{});
+  // (KS2: the second group's range may end in a ragged and a fully masked tile)
+  if constexpr (CAUSAL || KS2) run(j_split, j_end, T{});
   // iteration n_tiles-2: no S(j+2); the softmax of the last tile
   if (n_tiles >= 2) {
     const int j = n_tiles - 2;
@@ -838,13 +869,46 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if ((n_tiles - 1) & 1) iteration(n_tiles - 1, P1{}, F{}, F{}, F{}); else iteration(n_tiles - 1, P0{}, F{}, F{}, F{});
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
-  const float l_tot = wave_sum_halves(l_run);
-  const float l_rnd_tot = wave_sum_halves(l_rnd);
+  float l_tot = wave_sum_halves(l_run);
+  float l_rnd_tot = wave_sum_halves(l_rnd);
+  if constexpr (KS2) {
+    // the second key group hands (O, m, l, l~) of its keys to the first
+    // through LDS, which merges them as two blocks of the online softmax:
+    // m = max(m0, m1), a_g = 2^(m_g - m), O = a0 O0 + a1 O1, l = a0 l0 + a1 l1
+    __syncthreads();  // every wave is done with the K/V buffers
+    float* const xo0 = reinterpret_cast<float*>(seg_k0);  // O blocks 0, 1: [32 values][256 lanes]
+    float* const xo1 = reinterpret_cast<float*>(seg_k1);  // O blocks 2, 3
+    float* const xs = reinterpret_cast<float*>(seg_v0);   // m, l, l~: [3][256 lanes]
+    const int li = wr * 64 + lane;
+    if (kg_u == 1) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) (cb < 2 ? xo0 : xo1)[((cb & 1) * 16 + r) * 256 + li] = oacc[cb][r];
+      xs[li] = m_run;
+      xs[256 + li] = l_tot;
+      xs[512 + li] = l_rnd_tot;
+    }
+    __syncthreads();
+    if (kg_u == 1) return;
+    const float m1 = xs[li];
+    const float m = m_run > m1 ? m_run : m1;
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        oacc[cb][r] = oacc[cb][r] * a0 + (cb < 2 ? xo0 : xo1)[((cb & 1) * 16 + r) * 256 + li] * a1;
+    l_tot = l_tot * a0 + xs[256 + li] * a1;
+    l_rnd_tot = l_rnd_tot * a0 + xs[512 + li] * a1;
+    m_run = m;
+  }
   // l = 0 only for a row that sees no key (causal or all-(-inf) bias):
   // O = 0, LSE = -inf
-  constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS;
+  constexpr bool CAN_BE_EMPTY = CAUSAL || BIAS || KS2;
   const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_rnd_tot;
-  const int q = q0 + wave * 32 + c;
+  const int q = q0 + wr * 32 + c;
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
@@ -914,9 +978,9 @@ fa_fwd_merge_kernel(const float* __restrict__ Opart, const float* __restrict__ L
   if (t == 0) LSE[r] = m + __log2f(den) * 0.69314718055994530942f;
 }
 
-template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4>
+template <int DQK, int DV, int BC, bool NEG_SCALE, bool CAUSAL, bool BIAS, bool SPLIT, int NW = 4, bool KS2 = false>
 const void* kernel_ptr() {
-  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS, SPLIT, NW>;
+  return (const void*)&fa_fwd_kernel<DQK, DV, BC, NEG_SCALE, CAUSAL, BIAS, SPLIT, NW, KS2>;
 }
 
 // Grids of the 8-wave kernel: at least one 256-row workgroup per CU (MI355X
@@ -986,8 +1050,19 @@ int noalloc_scratch(void** ptr) {
   return 0;
 }
 
+// The in-workgroup key split (KS2): head size 128, no mask, no bias, no
+// split, a grid of 128-row workgroups that gives every CU at least one but
+// too few 256-row workgroups for the 8-wave kernel, and keys enough for each
+// group to run a few tiles.
+constexpr int64_t kKs2MinKeys = 1024;
+bool use_ks2(const LaunchArgs& a) {
+  return a.d == 128 && a.dv == 128 && !a.causal && a.bias == nullptr && a.n_splits <= 1 && a.Nk >= kKs2MinKeys &&
+         a.BH * ((a.Nq + 127) / 128) >= kSegMinWorkgroups;
+}
+
 int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
   const bool seg = use_seg(a);
+  const bool ks2 = !seg && use_ks2(a);
   const int br = seg ? 2 * BR : BR;
   const int n_qtiles = (int)((a.Nq + br - 1) / br);
   const int64_t nblk = a.BH * n_qtiles;
@@ -1012,7 +1087,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                   &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = seg && split ? (neg ? kernel_ptr<128, 128, 64, true, false, false, true, 8>()
+  const void* fn = ks2 ? (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8, true>()
+                            : kernel_ptr<128, 128, 64, false, false, false, false, 8, true>())
+                   : seg && split ? (neg ? kernel_ptr<128, 128, 64, true, false, false, true, 8>()
                                        : kernel_ptr<128, 128, 64, false, false, false, true, 8>())
                    : seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()
                                               : kernel_ptr<128, 128, 64, false, true, false, false, 8>())
@@ -1021,8 +1098,8 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                    : split ? select_pair<true>(a.d, a.dv, neg, a.causal, b)
                            : select_pair<false>(a.d, a.dv, neg, a.causal, b);
   if (fn == nullptr) return (int)hipErrorInvalidValue;
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nblk * n_splits)), dim3(seg ? 2 * NTHREADS : NTHREADS), args, 0,
-                                 stream);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(nblk * n_splits)), dim3(seg || ks2 ? 2 * NTHREADS : NTHREADS),
+                                 args, 0, stream);
   if (e != hipSuccess || !split) return e == hipSuccess ? 0 : (int)e;
   // merge the key ranges: DV / 4 threads per row
   const int64_t rows = a.BH * a.Nq;
@@ -1039,8 +1116,9 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v12: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
-         ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows), plain tiles without mask or bias in fixed MFMA segments (32 at "
+  return "gfx950 fa_fwd v13: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
+         ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
+         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "

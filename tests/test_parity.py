@@ -181,6 +181,31 @@ SEG_CASES = [
 ]
 
 
+# Shapes whose grid holds fewer than 256 workgroups of 256 rows but at least
+# 256 of 128 rows, with at least 1024 keys: the 8-wave kernel with two key
+# groups per workgroup (each attends to half of the key tiles, then the two
+# halves are merged in LDS).
+KS2_CASES = [
+    # B, H, Nq, Nk, seed, scale, kwargs, note
+    (1, 128, 256, 1024, 60, None, {}, "16 tiles, 8 per key group"),
+    (1, 128, 200, 1087, 61, None, {}, "17 tiles: ragged 17th, the second group's 9th tile past the keys"),
+    (2, 64, 256, 1100, 62, None, {}, "18 tiles, ragged last"),
+    (1, 128, 256, 2000, 63, -0.07, dict(k_scale=4.0, offset_frac=0.01, offset=8.0),
+     "negative scale, large logits (the 16K workload's recipe)"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,scale,kw,note", KS2_CASES)
+def test_key_group_kernel_full_compare(fa, B, H, Nq, Nk, seed, scale, kw, note):
+    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) and Nk >= 1024
+    say(f"case 8-wave key groups B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed, **kw)
+    sc = 1.0 / math.sqrt(128) if scale is None else scale
+    Og, Lg = run_gpu(fa, Q, K, V, sc)
+    Oo, Lo = oracle.attention(Q, K, V, sc)
+    check_parity(Og, Lg, Oo, Lo, f"8-wave key groups {note}")
+
+
 @pytest.mark.parametrize("B,H,Nq,Nk,seed,scale,kw,note", SEG_CASES)
 def test_eight_wave_kernel_full_compare(fa, B, H, Nq, Nk, seed, scale, kw, note):
     say(f"case 8-wave B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
