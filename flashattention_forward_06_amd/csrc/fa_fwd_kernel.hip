@@ -143,7 +143,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)),
                 "8-wave workgroups are built for the head-size-128 kernels without bias (key split: no mask)");
-  static_assert(!KS2 || (NW == 8 && !CAUSAL && !SPLIT), "the in-workgroup key split: 8 waves, no mask, no split");
+  static_assert(!KS2 || (NW == 8 && !SPLIT && !BIAS), "the in-workgroup key split: 8 waves, no bias, no split");
   constexpr int NWR = KS2 ? NW / 2 : NW;      // waves per key group (all waves without KS2)
   constexpr int BR = 32 * NWR;                // query rows per workgroup
   constexpr int KB = BC / 32;                 // 32-key MFMA blocks per tile
@@ -194,11 +194,21 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   if (CAUSAL) qt = n_qtiles - 1 - qt;  // the longest rows of a head start first
   const int q0 = qt * BR;
   // this workgroup's keys: [k0, k0 + Nk) of the head's Nk_all
-  // KS2: group g takes key tiles [g*G, (g+1)*G) of the head's ceil(Nk/BC),
-  // G = half of them rounded up; both groups run G iterations (the second
-  // group's last one may lie past Nk: fully masked, all weights 0), so every
-  // barrier is reached by all waves
-  const int ks_tiles = KS2 ? ((Nk_all + BC - 1) / BC + 1) / 2 : 0;
+  // KS2: group g takes key tiles [g*G, (g+1)*G) of the tiles the q-tile
+  // sees (all ceil(Nk/BC); with the causal mask those up to its last row's
+  // diagonal), G = half of them rounded up; both groups run G iterations
+  // (the second group's last one may lie past the visible keys: fully
+  // masked, all weights 0), so every barrier is reached by all waves
+  int ks_tiles = 0;
+  if constexpr (KS2) {
+    int total = (Nk_all + BC - 1) / BC;
+    if constexpr (CAUSAL) {
+      const int lim_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1 + Nk_all - Nq;
+      const int need = lim_last < 0 ? 0 : lim_last / BC + 1;
+      total = need < total ? need : total;
+    }
+    ks_tiles = (total + 1) / 2;
+  }
   const int k0 = SPLIT ? split * split_keys : (KS2 ? kg_u * ks_tiles * BC : 0);
   int Nk = SPLIT ? (Nk_all - k0 < split_keys ? Nk_all - k0 : split_keys) : Nk_all;
   if constexpr (KS2) Nk = Nk_all - k0 <= 0 ? 0 : (Nk_all - k0 < ks_tiles * BC ? Nk_all - k0 : ks_tiles * BC);
@@ -228,13 +238,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const int lim_last = q_last + off;  // the q-tile's last row sees keys <= lim_last
     const int lim_first = q0 + off;     // its first row sees keys <= lim_first
     const int need = lim_last < 0 ? 0 : lim_last / BC + 1;
-    n_tiles = need < n_tiles ? need : n_tiles;
+    if constexpr (!KS2) n_tiles = need < n_tiles ? need : n_tiles;  // KS2: G for both groups
     const int unmasked = lim_first + 1 <= 0 ? 0 : (lim_first + 1) / BC;
     first_masked = unmasked < first_masked ? unmasked : first_masked;
     const int my_lim = q0 + wr * 32 + c + off;
     key_lim = my_lim < key_lim ? my_lim : key_lim;
     if (n_tiles == 0) {
-      // no row of this q-tile sees any key: O = 0, LSE = -inf
+      // no row of this q-tile sees any key: O = 0, LSE = -inf (KS2: both
+      // groups come here together and write the same zeros)
       const int q = q0 + wr * 32 + c;
       constexpr uint32_t ORB = SPLIT ? 4 * DV : RBV;  // bytes per output row
 #pragma unroll
@@ -1050,13 +1061,12 @@ int noalloc_scratch(void** ptr) {
   return 0;
 }
 
-// The in-workgroup key split (KS2): head size 128, no mask, no bias, no
-// split, a grid of 128-row workgroups that gives every CU at least one but
+// The in-workgroup key split (KS2): head size 128, no bias, no split, a grid of 128-row workgroups that gives every CU at least one but
 // too few 256-row workgroups for the 8-wave kernel, and keys enough for each
 // group to run a few tiles.
 constexpr int64_t kKs2MinKeys = 1024;
 bool use_ks2(const LaunchArgs& a) {
-  return a.d == 128 && a.dv == 128 && !a.causal && a.bias == nullptr && a.n_splits <= 1 && a.Nk >= kKs2MinKeys &&
+  return a.d == 128 && a.dv == 128 && a.bias == nullptr && a.n_splits <= 1 && a.Nk >= kKs2MinKeys &&
          a.BH * ((a.Nq + 127) / 128) >= kSegMinWorkgroups;
 }
 
@@ -1087,8 +1097,10 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                   &opart, &lpart, &split_keys, &n_splits};
   const bool neg = a.scale < 0.0f;
   const bool b = bias != nullptr;
-  const void* fn = ks2 ? (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8, true>()
-                            : kernel_ptr<128, 128, 64, false, false, false, false, 8, true>())
+  const void* fn = ks2 ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8, true>()
+                                          : kernel_ptr<128, 128, 64, false, true, false, false, 8, true>())
+                                   : (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8, true>()
+                                          : kernel_ptr<128, 128, 64, false, false, false, false, 8, true>()))
                    : seg && split ? (neg ? kernel_ptr<128, 128, 64, true, false, false, true, 8>()
                                        : kernel_ptr<128, 128, 64, false, false, false, true, 8>())
                    : seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()

@@ -242,6 +242,34 @@ def test_causal_full_compare(fa, B, H, Nq, Nk, seed, note):
     check_parity(Og[~none], Lg[~none], Oo[~none], Lo[~none], f"causal {note}")
 
 
+# Causal launches of the same size class run the key groups too: each group
+# takes half of the tiles its q-tile sees, the second half holding the
+# diagonal; rows that see none of a group's keys get weight 0 in the merge.
+KS2_CAUSAL_CASES = [
+    # B, H, Nq, Nk, seed, note
+    (1, 128, 256, 1024, 86, "Nk > Nq: every row sees 768 keys and more"),
+    (1, 128, 200, 1087, 87, "ragged q and kv tails"),
+    (1, 32, 1280, 1024, 88, "Nq > Nk: the first 256 rows see no key, whole q-tiles empty"),
+    (2, 64, 256, 1100, 89, "two batches"),
+]
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,seed,note", KS2_CAUSAL_CASES)
+def test_causal_key_group_kernel_full_compare(fa, B, H, Nq, Nk, seed, note):
+    import torch
+    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) and Nk >= 1024
+    say(f"case causal 8-wave key groups B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
+    Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed)
+    o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(128), causal=True)
+    torch.cuda.synchronize()
+    Og, Lg = o_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    Oo, Lo = oracle.attention_masked(Q, K, V, 1 / math.sqrt(128), causal=True)
+    none = np.isneginf(Lo)
+    assert np.array_equal(np.isneginf(Lg), none), "rows that see no key must report LSE = -inf"
+    assert np.all(Og[none] == 0)
+    check_parity(Og[~none], Lg[~none], Oo[~none], Lo[~none], f"causal key groups {note}")
+
+
 def test_causal_offset_keys_sampled(fa):
     import torch
     say("case causal koffset: K*4, 1% rows +8, B=1 H=4 N=4096")
