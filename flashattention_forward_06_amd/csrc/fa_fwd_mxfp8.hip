@@ -74,23 +74,32 @@ __device__ inline intx8 lds_read32(const char* p0, const char* p1) {
   return intx8{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
 }
 
-template <bool NEG_SCALE, bool CAUSAL, int NW>
+// KS2 (8 waves only): two groups of 4 waves attend to the two halves of the
+// key tiles that 128 query rows see and merge (O, m, l) through LDS at the
+// end, for launches that give each CU one 128-row workgroup but too few
+// 256-row ones.
+template <bool NEG_SCALE, bool CAUSAL, int NW, bool KS2 = false>
 __global__ void __launch_bounds__(64 * NW)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ Qs,
                     const uint8_t* __restrict__ K8, const uint8_t* __restrict__ Ks,
                     const uint8_t* __restrict__ Vt8, const uint8_t* __restrict__ Vs,
                     uint16_t* __restrict__ O, float* __restrict__ LSE,
-                    int Nq, int Nk, int ldv, int n_qtiles, float c_log2) {
+                    int Nq, int Nk_all, int ldv, int n_qtiles, float c_log2) {
+  static_assert(!KS2 || NW == 8, "key groups: 8 waves");
   constexpr int KB = 2;  // 32-key blocks per tile
-  constexpr int BR = 32 * NW;  // query rows per workgroup
-  __shared__ __attribute__((aligned(1024))) char smem[MX_LDS];
+  constexpr int NWR = KS2 ? NW / 2 : NW;  // waves per key group (all waves without KS2)
+  constexpr int BR = 32 * NWR;  // query rows per workgroup
+  constexpr int NKG = KS2 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char smem[NKG * MX_LDS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int c = lane & 31;
   const int h = lane >> 5;
+  const int wr = KS2 ? (wave & (NWR - 1)) : wave;  // which 32 rows of the workgroup
+  const int kg_u = KS2 ? __builtin_amdgcn_readfirstlane(wave / NWR) : 0;  // key group
 
   int bh, qt;
   if constexpr (CAUSAL) {
@@ -106,28 +115,48 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   }
   const int q0 = qt * BR;
 
-  const size_t bq = (size_t)bh * (size_t)Nq, bk = (size_t)bh * (size_t)Nk;
+  // KS2: group g takes key tiles [g*G, (g+1)*G) of the tiles the q-tile sees,
+  // G = half of them rounded up; both groups run G iterations (tiles past the
+  // visible keys are fully masked), so every barrier is reached by all waves
+  int ks_tiles = 0;
+  if constexpr (KS2) {
+    int total = (Nk_all + MX_BC - 1) / MX_BC;
+    if constexpr (CAUSAL) {
+      const int lim_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1 + Nk_all - Nq;
+      const int need = lim_last < 0 ? 0 : lim_last / MX_BC + 1;
+      total = need < total ? need : total;
+    }
+    ks_tiles = (total + 1) / 2;
+  }
+  const int k0 = KS2 ? kg_u * ks_tiles * MX_BC : 0;  // this group's first key
+  const int Nk = KS2 ? (Nk_all - k0 <= 0 ? 0 : (Nk_all - k0 < ks_tiles * MX_BC ? Nk_all - k0 : ks_tiles * MX_BC))
+                     : Nk_all;
+  const int vrest = ldv - k0 > 0 ? ldv - k0 : 0;  // V^T columns from k0 on
+
+  const size_t bq = (size_t)bh * (size_t)Nq, bk = (size_t)bh * (size_t)Nk_all + (size_t)k0;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q8 + bq * D, (uint32_t)Nq * D);
   const __amdgpu_buffer_rsrc_t rqs = make_rsrc(Qs + bq * 4, (uint32_t)Nq * 4u);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(K8 + bk * D, (uint32_t)Nk * D);
-  const __amdgpu_buffer_rsrc_t rks = make_rsrc(Ks + (size_t)bh * (size_t)ldv * 4, (uint32_t)Nk * 4u);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vt8 + (size_t)bh * D * (size_t)ldv, (uint32_t)D * (uint32_t)ldv);
-  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(Vs + (size_t)bh * (size_t)(ldv / 32) * D, (uint32_t)(ldv / 32) * D);
+  const __amdgpu_buffer_rsrc_t rks = make_rsrc(Ks + ((size_t)bh * (size_t)ldv + (size_t)k0) * 4, (uint32_t)Nk * 4u);
+  const __amdgpu_buffer_rsrc_t rv =
+      make_rsrc(Vt8 + (size_t)bh * D * (size_t)ldv + (size_t)k0, (uint32_t)D * (uint32_t)ldv - (uint32_t)(ldv - vrest));
+  const __amdgpu_buffer_rsrc_t rvs = make_rsrc(Vs + ((size_t)bh * (size_t)(ldv / 32) + (size_t)(k0 / 32)) * D,
+                                               (uint32_t)(vrest / 32) * D);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + bq * D, (uint32_t)Nq * ROW_BYTES);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int wr_u = __builtin_amdgcn_readfirstlane(wr);
 
   const int n_full = Nk / MX_BC;
-  int n_tiles = n_full + (Nk % MX_BC != 0);
+  int n_tiles = KS2 ? ks_tiles : n_full + (Nk % MX_BC != 0);
   int first_masked = n_full;
   int key_lim = Nk - 1;
-  const int q = q0 + wave * 32 + c;
+  const int q = q0 + wr * 32 + c;
   if constexpr (CAUSAL) {
-    const int off = Nk - Nq;
+    const int off = Nk_all - k0 - Nq;  // key k0 + j is hidden from query i when j > i + off
     const int q_last = (q0 + BR < Nq ? q0 + BR : Nq) - 1;
     const int lim_last = q_last + off;
     const int lim_first = q0 + off;
     const int need = lim_last < 0 ? 0 : lim_last / MX_BC + 1;
-    n_tiles = need < n_tiles ? need : n_tiles;
+    if constexpr (!KS2) n_tiles = need < n_tiles ? need : n_tiles;  // KS2: G for both groups
     const int unmasked = lim_first + 1 <= 0 ? 0 : (lim_first + 1) / MX_BC;
     first_masked = unmasked < first_masked ? unmasked : first_masked;
     key_lim = q + off < key_lim ? q + off : key_lim;
@@ -143,8 +172,8 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
 
   // LDS: K(j+2), K(j+3) tiles then V(j), V(j+1), each followed by its 256
   // scale bytes (K: 64 keys x 4 blocks; V: 2 key blocks x 128 rows).
-  char* const kst0 = smem;
-  char* const vst0 = smem + 2 * MX_STAGE;
+  char* const kst0 = smem + kg_u * MX_LDS;
+  char* const vst0 = kst0 + 2 * MX_STAGE;
   auto kbuf = [&](int i) FA_INLINE { return kst0 + i * MX_STAGE; };
   auto vbuf = [&](int i) FA_INLINE { return vst0 + i * MX_STAGE; };
 
@@ -152,14 +181,14 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   auto k_to_lds = [&](int j, char* dst) FA_INLINE {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)MX_KTILE);
 #pragma unroll
-    for (int i = 0; i < 8 / NW; ++i) {
-      const uint32_t blk = (uint32_t)(i * NW + wave_u);  // 1 KiB = 8 rows
+    for (int i = 0; i < 8 / NWR; ++i) {
+      const uint32_t blk = (uint32_t)(i * NWR + wr_u);  // 1 KiB = 8 rows
       const uint32_t row = blk * 8u + ((uint32_t)lane >> 3);
       const uint32_t ch = ((uint32_t)lane & 7u) ^ kx(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)((lds_char*)dst + blk * 1024u),
                                                16, row * MX_KROW + ch * 16u, soff, 0, 0);
     }
-    if (wave_u == 2 && lane < 16)
+    if (wr_u == 2 && lane < 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rks, (__attribute__((address_space(3))) void*)((lds_char*)dst + MX_KTILE),
                                                16, (uint32_t)lane * 16u,
                                                __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)(MX_BC * 4)), 0, 0);
@@ -169,14 +198,14 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   auto v_to_lds = [&](int j, char* dst) FA_INLINE {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)j * (uint32_t)MX_BC);
 #pragma unroll
-    for (int i = 0; i < 8 / NW; ++i) {
-      const uint32_t blk = (uint32_t)(i * NW + wave_u);  // 1 KiB = 16 rows
+    for (int i = 0; i < 8 / NWR; ++i) {
+      const uint32_t blk = (uint32_t)(i * NWR + wr_u);  // 1 KiB = 16 rows
       const uint32_t row = blk * 16u + ((uint32_t)lane >> 2);
       const uint32_t ch = ((uint32_t)lane & 3u) ^ vx(row);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)((lds_char*)dst + blk * 1024u),
                                                16, row * (uint32_t)ldv + ch * 16u, soff, 0, 0);
     }
-    if (wave_u == 3 && lane < 16)
+    if (wr_u == 3 && lane < 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rvs, (__attribute__((address_space(3))) void*)((lds_char*)dst + MX_VTILE),
                                                16, (uint32_t)lane * 16u,
                                                __builtin_amdgcn_readfirstlane((uint32_t)j * 2u * (uint32_t)D), 0, 0);
@@ -522,7 +551,8 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   int j_split = first_masked - 1;
   j_split = j_split < 0 ? 0 : (j_split > j_end ? j_end : j_split);
   run(0, j_split, F{});
-  if constexpr (CAUSAL) run(j_split, j_end, T{});
+  // (KS2: the second group's range may end in a ragged and a fully masked tile)
+  if constexpr (CAUSAL || KS2) run(j_split, j_end, T{});
   if (n_tiles >= 2) {
     const int j = n_tiles - 2;
     const bool mask = n_tiles - 1 >= first_masked;
@@ -534,12 +564,41 @@ fa_fwd_mxfp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ 
   }
   if ((n_tiles - 1) & 1) iteration(n_tiles - 1, P1{}, F{}, F{}, F{}); else iteration(n_tiles - 1, P0{}, F{}, F{}, F{});
 
-  const float l_tot = wave_sum_halves(l_run);
-  const float inv_l = (CAUSAL && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
+  float l_tot = wave_sum_halves(l_run);
+  if constexpr (KS2) {
+    // the second key group hands (O, m, l) of its keys to the first through
+    // LDS: m = max(m0, m1), a_g = 2^(m_g - m), O = a0 O0 + a1 O1, l = a0 l0 + a1 l1
+    __syncthreads();  // every wave is done with the K/V stages
+    float* const xo = reinterpret_cast<float*>(smem);  // [64 values][256 lanes]
+    float* const xs = xo + 64 * 256;                  // m, l: [2][256 lanes]
+    const int li = wr * 64 + lane;
+    if (kg_u == 1) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xo[(cb * 16 + r) * 256 + li] = oacc[cb][r];
+      xs[li] = m_run;
+      xs[256 + li] = l_tot;
+    }
+    __syncthreads();
+    if (kg_u == 1) return;
+    const float m1 = xs[li];
+    const float m = m_run > m1 ? m_run : m1;
+    const float a0 = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[cb][r] = oacc[cb][r] * a0 + xo[(cb * 16 + r) * 256 + li] * a1;
+    l_tot = l_tot * a0 + xs[256 + li] * a1;
+    m_run = m;
+  }
+  constexpr bool CAN_BE_EMPTY = CAUSAL || KS2;  // a row may see no key (of a group)
+  const float inv_l = (CAN_BE_EMPTY && l_tot == 0.0f) ? 0.0f : 1.0f / l_tot;
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) store_bf16_row_block(ro, (uint32_t)q, cb, h, oacc[cb], inv_l);
   if (h == 0 && q < Nq)
-    LSE[bq + q] = (CAUSAL && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
+    LSE[bq + q] = (CAN_BE_EMPTY && l_tot == 0.0f) ? -__builtin_inff() : (m_run + __log2f(l_tot)) * 0.69314718055994530942f;
 }
 
 
@@ -643,9 +702,10 @@ __global__ void __launch_bounds__(256) mx_quantize_vt_kernel(const uint16_t* __r
 constexpr int64_t kMx8WaveMinWorkgroups = 256;
 
 namespace {
-template <int NW>
+template <int NW, bool KS2 = false>
 int launch_mxfp8_nw(const MxArgs& a, hipStream_t stream) {
-  int n_qtiles = (int)((a.Nq + 32 * NW - 1) / (32 * NW));
+  constexpr int BR = KS2 ? 16 * NW : 32 * NW;  // query rows per workgroup
+  int n_qtiles = (int)((a.Nq + BR - 1) / BR);
   const float c_log2 = (float)((double)a.scale * 1.4426950408889634074);
   const uint8_t *q = static_cast<const uint8_t*>(a.Q8), *qs = static_cast<const uint8_t*>(a.Qs);
   const uint8_t *k = static_cast<const uint8_t*>(a.K8), *ks = static_cast<const uint8_t*>(a.Ks);
@@ -656,8 +716,10 @@ int launch_mxfp8_nw(const MxArgs& a, hipStream_t stream) {
   float cl = c_log2;
   void* args[] = {&q, &qs, &k, &ks, &v, &vs, &o, &lse, &nq, &nk, &ldv, &n_qtiles, &cl};
   const bool neg = a.scale < 0.0f;
-  const void* fn = a.causal ? (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, true, NW> : (const void*)&fa_fwd_mxfp8_kernel<false, true, NW>)
-                            : (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, false, NW> : (const void*)&fa_fwd_mxfp8_kernel<false, false, NW>);
+  const void* fn = a.causal ? (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, true, NW, KS2>
+                                    : (const void*)&fa_fwd_mxfp8_kernel<false, true, NW, KS2>)
+                            : (neg ? (const void*)&fa_fwd_mxfp8_kernel<true, false, NW, KS2>
+                                    : (const void*)&fa_fwd_mxfp8_kernel<false, false, NW, KS2>);
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)(a.BH * n_qtiles)), dim3(64 * NW), args, 0, stream);
   return e == hipSuccess ? 0 : (int)e;
 }
@@ -666,7 +728,11 @@ int launch_mxfp8_nw(const MxArgs& a, hipStream_t stream) {
 
 int launch_fa_fwd_mxfp8(const MxArgs& a, hipStream_t stream) {
   const int64_t wg8 = a.BH * ((a.Nq + 255) / 256);
-  return wg8 >= kMx8WaveMinWorkgroups ? launch_mxfp8_nw<8>(a, stream) : launch_mxfp8_nw<4>(a, stream);
+  if (wg8 >= kMx8WaveMinWorkgroups) return launch_mxfp8_nw<8>(a, stream);
+  // two key groups of 4 waves on 128 rows where 128-row workgroups give every
+  // CU one and the keys are long enough for both groups to run a few tiles
+  if (a.BH * ((a.Nq + 127) / 128) >= kMx8WaveMinWorkgroups && a.Nk >= 1024) return launch_mxfp8_nw<8, true>(a, stream);
+  return launch_mxfp8_nw<4>(a, stream);
 }
 
 int launch_mx_quantize_rows(const void* X, void* E, void* S, int64_t BH, int64_t N, int64_t ldS, hipStream_t stream) {

@@ -173,6 +173,12 @@ MX_CASES = [
     (2, 128, 300, 520, False, 720, "8 waves: ragged q tile (44 rows), ragged keys"),
     (1, 256, 256, 1000, False, 721, "8 waves: six segmented iteration pairs, 40-key tail"),
     (2, 128, 512, 512, True, 722, "8 waves: causal"),
+    # fewer than 256 workgroups of 256 rows, at least 256 of 128, >= 1024 keys:
+    # two key groups of 4 waves per workgroup, merged in LDS
+    (1, 128, 256, 1024, False, 730, "key groups: 8 tiles each"),
+    (1, 128, 200, 1087, False, 731, "key groups: ragged 17th tile, the second group's 9th past the keys"),
+    (1, 128, 256, 1100, True, 732, "key groups, causal"),
+    (1, 32, 1280, 1024, True, 733, "key groups, causal, Nq > Nk: whole q-tiles see no key"),
 ]
 
 
