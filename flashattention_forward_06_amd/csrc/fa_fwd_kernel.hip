@@ -1061,13 +1061,17 @@ int noalloc_scratch(void** ptr) {
   return 0;
 }
 
-// The in-workgroup key split (KS2): head size 128, no bias, no split, a grid of 128-row workgroups that gives every CU at least one but
-// too few 256-row workgroups for the 8-wave kernel, and keys enough for each
-// group to run a few tiles.
+// The in-workgroup key split (KS2): head size 128, no bias, no split, keys
+// enough for each group to run a few tiles, and a grid of 256 to 512
+// 128-row workgroups (one or two per CU) that does not take the 256-row
+// 8-wave kernel.  Causal, in one process against the 4-wave kernel: 256
+// workgroups +23-30 %, 384 +38 %, 512 +15 %, 640 -6 %, 768 -9 to -11 %,
+// 1024 and more -6 to -19 %.
 constexpr int64_t kKs2MinKeys = 1024;
 bool use_ks2(const LaunchArgs& a) {
+  const int64_t g128 = a.BH * ((a.Nq + 127) / 128);
   return a.d == 128 && a.dv == 128 && a.bias == nullptr && a.n_splits <= 1 && a.Nk >= kKs2MinKeys &&
-         a.BH * ((a.Nq + 127) / 128) >= kSegMinWorkgroups;
+         g128 >= kSegMinWorkgroups && g128 <= 2 * kSegMinWorkgroups;
 }
 
 int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {

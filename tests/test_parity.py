@@ -197,7 +197,7 @@ KS2_CASES = [
 
 @pytest.mark.parametrize("B,H,Nq,Nk,seed,scale,kw,note", KS2_CASES)
 def test_key_group_kernel_full_compare(fa, B, H, Nq, Nk, seed, scale, kw, note):
-    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) and Nk >= 1024
+    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) <= 512 and Nk >= 1024
     say(f"case 8-wave key groups B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
     Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed, **kw)
     sc = 1.0 / math.sqrt(128) if scale is None else scale
@@ -257,7 +257,7 @@ KS2_CAUSAL_CASES = [
 @pytest.mark.parametrize("B,H,Nq,Nk,seed,note", KS2_CAUSAL_CASES)
 def test_causal_key_group_kernel_full_compare(fa, B, H, Nq, Nk, seed, note):
     import torch
-    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) and Nk >= 1024
+    assert B * H * ((Nq + 255) // 256) < 256 <= B * H * ((Nq + 127) // 128) <= 512 and Nk >= 1024
     say(f"case causal 8-wave key groups B={B} H={H} Nq={Nq} Nk={Nk} seed={seed} ({note})")
     Q, K, V = fi.make_qkv(B, H, Nq, Nk, 128, seed=seed)
     o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=1 / math.sqrt(128), causal=True)
