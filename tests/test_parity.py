@@ -320,6 +320,19 @@ def test_causal_eight_wave_scales(fa, scale, note):
     check_parity(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Oo, Lo, f"causal 8-wave {note}")
 
 
+@pytest.mark.parametrize("scale,note", [(-1 / math.sqrt(128), "negative scale"), (0.0, "zero scale")])
+def test_key_group_kernel_scales(fa, scale, note):
+    import torch
+    say(f"case 8-wave key groups B=1 H=128 Nq=256 Nk=1100 scale={scale} ({note}), causal and not")
+    Q, K, V = fi.make_qkv(1, 128, 256, 1100, 128, seed=93)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd(to_dev(Q), to_dev(K), to_dev(V), scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        Oo, Lo = oracle.attention_masked(Q, K, V, scale, causal=causal)
+        check_parity(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Oo, Lo,
+                     f"key groups {note} causal={causal}")
+
+
 def test_causal_eight_wave_offset_keys_sampled(fa):
     import torch
     w = fi.WORKLOADS["b1_h16_n16384_koffset"]

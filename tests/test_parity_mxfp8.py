@@ -205,6 +205,18 @@ def test_mxfp8_scale_variants(fa, scale, note):
 
 
 @pytest.mark.parametrize("scale,note", [(-0.09, "negative scale"), (0.0, "zero scale")])
+def test_mxfp8_key_group_scales(fa, scale, note):
+    import torch
+    say(f"case mxfp8 key groups B=1 H=128 Nq=256 Nk=1100 scale={scale} ({note})")
+    dev, (Qd, Kd, Vd) = mx_case(1, 128, 256, 1100, 734)
+    for causal in (False, True):
+        o, lse = fa.fa_fwd_mxfp8(*dev, 1100, scale=scale, causal=causal)
+        torch.cuda.synchronize()
+        check_mx(o_to_f64(o), lse.cpu().numpy().astype(np.float64), Qd, Kd, Vd, scale, causal,
+                 f"key groups {note} causal={causal}")
+
+
+@pytest.mark.parametrize("scale,note", [(-0.09, "negative scale"), (0.0, "zero scale")])
 def test_mxfp8_eight_wave_scales(fa, scale, note):
     import torch
     say(f"case mxfp8 8-wave B=1 H=256 Nq=256 Nk=520 scale={scale} ({note})")
