@@ -90,8 +90,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--also", default=None,
                    help="comma-separated further workloads timed after the main one and reported under "
-                        "'also' (default: the 16K workload when the main one is the default plain forward; "
-                        "'none' for none)")
+                        "'also' (default: the 16K workload and the 5090 benchmark shape when the main one is "
+                        "the default plain forward; 'none' for none)")
     p.add_argument("--no-clock", action="store_true",
                    help="skip the sustained run that samples the shader clock")
     p.add_argument("--splitkv", type=int, default=None, metavar="N",
@@ -471,7 +471,7 @@ def main():
         out["clock"] = sustained_clock(step)
     also = args.also
     if also is None:
-        also = "b1_h16_n16384_koffset" if plain and w.name == DEFAULT_WORKLOAD else "none"
+        also = "b1_h16_n16384_koffset,rtx5090_q4096_kv8192" if plain and w.name == DEFAULT_WORKLOAD else "none"
     failures = []
     if also != "none":
         if not plain:
@@ -491,7 +491,10 @@ def main():
                 if rc != 0:
                     raise fa.FaError(rc, fa.fa_status_string(rc))
 
-            ms = time_calls(step_a, stream, args.steps, args.warmup)
+            # the clock has dropped during the previous workload's host-side
+            # parity check: warm up for ~40 ms of calls however short a call is
+            est = time_calls(step_a, stream, 5, 1)
+            ms = time_calls(step_a, stream, args.steps, max(args.warmup, int(40.0 / max(est, 1e-3))))
             fl = wa.flops
             rec = {"TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2), "frac": round(fl / (ms * 1e-3) / 1e12 / peak, 4),
                    "kernel_ms": round(ms, 4), "steps": args.steps, "warmup": args.warmup, "flop_per_step": fl}
