@@ -49,7 +49,7 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # bias kernel and the key split; the 8-wave kernel that the default workload
 # runs compiles to the same machine code as when it was measured.)
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v13: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids "
+    "kernel": "gfx950 fa_fwd v14: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids "
               "of >= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key "
               "groups of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA "
               "segments (32 at head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline (S two tiles "

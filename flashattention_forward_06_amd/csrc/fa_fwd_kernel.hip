@@ -141,8 +141,9 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // At head size 64 (16 MFMAs per tile, two scores per segment): +2 % at
   // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.
   constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
-  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)),
-                "8-wave workgroups are built for the head-size-128 kernels without bias (key split: no mask)");
+  static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)) ||
+                    (NW == 8 && DQK == 64 && DV == 64 && BC == 64 && !BIAS && !CAUSAL && !SPLIT && !KS2),
+                "8-wave workgroups: head size 128 without bias (key split: no mask), 64 without mask or bias");
   static_assert(!KS2 || (NW == 8 && !SPLIT && !BIAS), "the in-workgroup key split: 8 waves, no bias, no split");
   constexpr int NWR = KS2 ? NW / 2 : NW;      // waves per key group (all waves without KS2)
   constexpr int BR = 32 * NWR;                // query rows per workgroup
@@ -1005,7 +1006,9 @@ constexpr int64_t kSegMinWorkgroups = 256;
 constexpr int64_t kSegCausalMinRows = 8192;
 bool use_seg(const LaunchArgs& a) {
   const int64_t ranges = a.n_splits > 1 ? a.n_splits : 1;
-  if (a.d != 128 || a.dv != 128 || a.bias != nullptr) return false;
+  if (a.bias != nullptr) return false;
+  if (a.d == 64 && a.dv == 64) return !a.causal && ranges == 1 && a.BH * ((a.Nq + 255) / 256) >= kSegMinWorkgroups;
+  if (a.d != 128 || a.dv != 128) return false;
   if (a.causal && (ranges > 1 || a.Nq < kSegCausalMinRows)) return false;
   return a.BH * ((a.Nq + 255) / 256) * ranges >= kSegMinWorkgroups;
 }
@@ -1105,6 +1108,8 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
                                           : kernel_ptr<128, 128, 64, false, true, false, false, 8, true>())
                                    : (neg ? kernel_ptr<128, 128, 64, true, false, false, false, 8, true>()
                                           : kernel_ptr<128, 128, 64, false, false, false, false, 8, true>()))
+                   : seg && a.d == 64 ? (neg ? kernel_ptr<64, 64, 64, true, false, false, false, 8>()
+                                             : kernel_ptr<64, 64, 64, false, false, false, false, 8>())
                    : seg && split ? (neg ? kernel_ptr<128, 128, 64, true, false, false, true, 8>()
                                        : kernel_ptr<128, 128, 64, false, false, false, true, 8>())
                    : seg   ? (a.causal ? (neg ? kernel_ptr<128, 128, 64, true, true, false, false, 8>()
@@ -1132,7 +1137,7 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v13: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias on grids of "
+  return "gfx950 fa_fwd v14: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
          "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "

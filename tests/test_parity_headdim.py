@@ -32,6 +32,10 @@ CASES = [
     (64, 64, 2, 3, 200, 333, False, 401, "ragged"),
     (64, 64, 1, 2, 300, 130, True, 402, "causal, Nq > Nk"),
     (64, 64, 1, 1, 129, 65, True, 403, "causal, one row / key past a tile"),
+    # >= 256 workgroups of 256 rows without mask: 8-wave workgroups
+    (64, 64, 1, 256, 300, 200, False, 409, "8 waves: ragged q tile (44 rows) and kv tail"),
+    (64, 64, 2, 128, 256, 1000, False, 410, "8 waves: seven segmented iteration pairs, ragged kv"),
+    (64, 64, 1, 256, 1, 64, False, 411, "8 waves: one query row per head, one kv tile"),
     (256, 256, 1, 2, 256, 256, False, 404, "tile aligned"),
     (256, 256, 2, 3, 200, 333, False, 405, "ragged"),
     (256, 256, 1, 2, 300, 130, True, 406, "causal, Nq > Nk"),
