@@ -364,6 +364,25 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   float m_run = -__builtin_inff();  // running max, log2 units, per query
   float l_run = 0.0f;               // partial row sum of this lane's keys (fp32 P, for LSE)
   float l_rnd = 0.0f;               // the same over the bf16-rounded P (normalises O)
+  // With RSUM_MFMA the rounded-P sum is taken on the matrix core instead of
+  // with bf16 dot products (each of which holds the SIMD about as long as
+  // half an MFMA): next to each P V product, a 16x16x32 product of a 0/1 mask
+  // with the same P fragment.  That product reads the fragment's lane
+  // n + 16 g as column n % 16, k group g; the query of lane L is L % 32, so
+  // mask row 0 (and 8) over the even groups sums query n and row 4 (and 12)
+  // over the odd groups query n + 16.  Output register 0 of lane L is then
+  // the rounded sum of query L % 32 over every key so far (registers 1-3
+  // stay 0): it accumulates and is rescaled exactly as O is.  Off where its
+  // 8 registers make the kernel spill much more: head size 256 with a bias,
+  // and (192, 128) without mask or bias (-17 % there; +3-6 % elsewhere).
+  constexpr bool RSUM_MFMA = !(DQK == 256 && BIAS) && !(DQK == 192 && !CAUSAL && !BIAS);
+  floatx4 lt{0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 rmask;
+  {
+    const __bf16 one = ((lane & 3) == 0 && ((lane >> 2) & 1) == ((lane >> 4) & 1)) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rmask[i] = one;
+  }
 
   // S^T = K Q^T for the BC keys of one K buffer (32-key blocks).
   // The K fragments of k step t + KPF are read before the MFMAs of step t
@@ -407,13 +426,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // Row sum of one tile's P as rounded to bf16, i.e. of the weights the P V
-  // product actually uses.  O is divided by this sum, so the weights of every
+  // product actually uses (where RSUM_MFMA is off).  O is divided by this sum, so the weights of every
   // output row sum to 1 whatever the rounding of P; the fp32 sum of the
   // unrounded P (l_run) gives the log-sum-exp.  With the running max kept
   // stale, the largest P of a row is no longer exactly 1 and carries a bf16
   // rounding error; dividing by the unrounded sum would leave that error
   // (up to 2^-8 of |v|) in the output.
   auto rounded_sum = [&](const bf16x8 (&pb)[2 * KB]) FA_INLINE -> float {
+    if constexpr (RSUM_MFMA) return 0.0f;
     float acc = 0.0f;
     const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
@@ -527,6 +547,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const uintx2 hi2 = __builtin_bit_cast(uintx2, hi);
         const bf16x8 a = __builtin_bit_cast(bf16x8, uintx4{lo2.x, lo2.y, hi2.x, hi2.y});
         oacc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[ks4], oacc[cb], 0, 0, 0);
+        if (RSUM_MFMA && cb == NCB - 1) lt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rmask, pb[ks4], lt, 0, 0, 0);
       }
     }
   };
@@ -640,6 +661,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     for (int i = 0; i < NCB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+    if constexpr (RSUM_MFMA) lt[0] *= alpha;
   };
 
   // ---- tiles 0 and 1: P(0) and S(1) before the loop.
@@ -780,7 +802,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       const bf16x2 pr{(__bf16)pe[r], (__bf16)pe[r + 1]};
       pn[r >> 3][r & 7] = pr[0];
       pn[r >> 3][(r & 7) + 1] = pr[1];
-      lrnd = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lrnd, false);
+      if constexpr (!RSUM_MFMA) lrnd = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lrnd, false);
     };
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
@@ -808,6 +830,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         const int m = i - NS;
         oacc[m & (NCB - 1)] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[m % (PF + 1)], pb[m >> CSH], oacc[m & (NCB - 1)], 0, 0, 0);
+        if (RSUM_MFMA && (m & (NCB - 1)) == NCB - 1)
+          lt = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rmask, pb[m >> CSH], lt, 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -882,7 +906,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 
   // ---- epilogue: 1/l, bf16 (round to nearest even), LSE in natural log.
   float l_tot = wave_sum_halves(l_run);
-  float l_rnd_tot = wave_sum_halves(l_rnd);
+  float l_rnd_tot = RSUM_MFMA ? lt[0] : wave_sum_halves(l_rnd);
   if constexpr (KS2) {
     // the second key group hands (O, m, l, l~) of its keys to the first
     // through LDS, which merges them as two blocks of the online softmax:
@@ -1137,14 +1161,16 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v14: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
+  return "gfx950 fa_fwd v15: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
          "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
          "per SIMD and a two-FMA exponent at head size 64 with a bias), "
-         "V^T via ds_read_b64_tr_b16; no tile max unless exp2 exceeds 2^16; causal tile skipping; "
+         "V^T via ds_read_b64_tr_b16; O divided by the sum of the bf16 P taken on mfma_f32_16x16x32_bf16 with a 0/1 mask "
+         "(bf16 dot products at head size 256 with a bias and (192, 128) without mask or bias); "
+         "no tile max unless exp2 exceeds 2^16; causal tile skipping; "
          "fp32 additive bias; key split with LSE merge";
 }
 
