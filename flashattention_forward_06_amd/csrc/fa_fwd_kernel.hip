@@ -790,12 +790,21 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     s2[0] = floatx16{};
     s2[1] = floatx16{};
     bf16x8 kf[PF + 1], vf[PF + 1], pn[2 * KB];
-    float pe[32];
+    float pe[32], xe[32];
     float lsum = 0.0f, lrnd = 0.0f;
     const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
-    auto score = [&](int r) FA_INLINE {  // score r of this lane: key block r >> 4, row r & 15
-      pe[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run));
-      lsum += pe[r];
+    // score r of this lane (key block r >> 4, row r & 15) in three steps, each
+    // a segment after the one before, so that no VALU instruction waits for
+    // the result of the one just issued: the exponent, the exponential, the
+    // row sum
+    auto st_fma = [&](int r) FA_INLINE {
+      if (r < 32) xe[r] = __builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run);
+    };
+    auto st_exp = [&](int r) FA_INLINE {
+      if (r < 32) pe[r] = __builtin_amdgcn_exp2f(xe[r]);
+    };
+    auto st_add = [&](int r) FA_INLINE {
+      if (r < 32) lsum += pe[r];
     };
     auto pack = [&](int q) FA_INLINE {  // scores 2q, 2q + 1 -> bf16 (RNE), and their rounded sum
       const int r = 2 * q;
@@ -807,20 +816,26 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
 #pragma unroll
-    for (int r = 0; r < AHEAD; ++r) score(r);
+    for (int r = 0; r < SPS * (AHEAD + 1); ++r) st_fma(r);
+#pragma unroll
+    for (int r = 0; r < SPS * AHEAD; ++r) st_exp(r);
+#pragma unroll
+    for (int r = 0; r < SPS * (AHEAD - 1); ++r) st_add(r);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       const int nxt = i + PF;  // the MFMA whose operand is read in this segment
       if (nxt < NS) kf[nxt % (PF + 1)] = kfrag(nxt);
       else if (nxt < NM) vf[(nxt - NS) % (PF + 1)] = vfrag(nxt - NS);
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) st_fma(SPS * (i + AHEAD + 1) + u);
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) st_exp(SPS * (i + AHEAD) + u);
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) st_add(SPS * (i + AHEAD - 1) + u);
       if constexpr (SPS == 1) {
-        if (i + AHEAD < 32) score(i + AHEAD);
         if (i & 1) pack(i >> 1);
       } else {
-#pragma unroll
-        for (int u = 0; u < SPS; ++u)
-          if (SPS * i + u + AHEAD < 32) score(SPS * i + u + AHEAD);
 #pragma unroll
         for (int u = 0; u < SPS / 2; ++u) pack(i * (SPS / 2) + u);
       }
@@ -1161,11 +1176,12 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v15: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
+  return "gfx950 fa_fwd v16: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
          "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA segments (32 at "
          "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
-         "(S two tiles ahead of P V, softmax in between), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
+         "(S two tiles ahead of P V, softmax in between, its exponent, exponential and row sum a segment apart), "
+         "direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
          "per SIMD and a two-FMA exponent at head size 64 with a bias), "
          "V^T via ds_read_b64_tr_b16; O divided by the sum of the bf16 P taken on mfma_f32_16x16x32_bf16 with a 0/1 mask "
