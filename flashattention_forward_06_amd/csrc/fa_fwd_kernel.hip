@@ -134,13 +134,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // tiles on the diagonal keep the masked iteration).
   constexpr bool SEG = NW == 8;
   // The segmented iteration also runs the plain tiles of the 4-wave head-size-
-  // 128 kernels without mask or bias (including the key split): +6.5 % on a
-  // grid of one workgroup per CU (B=1, H=8, Nq=4096, Nk=8192), identical
-  // results.  With the causal mask it gained there too (+5 %) but lost 1 % on
-  // the 16K-token workload, so the causal kernels keep the plain iteration.
+  // 128 kernels without a bias (including the key split): +6.5 % on a grid
+  // of one workgroup per CU (B=1, H=8, Nq=4096, Nk=8192), identical results.
   // At head size 64 (16 MFMAs per tile, two scores per segment): +2 % at
-  // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.
-  constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !CAUSAL && !BIAS) || SEG;
+  // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.  With the
+  // causal mask (the tiles below the diagonal; causal launches of 8192 rows
+  // or more run 8 waves): +4 to +5.5 % at 2048 and 4096 rows, +3 % at head
+  // size 64 and 8192 rows.
+  constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !BIAS) || SEG;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)) ||
                     (NW == 8 && DQK == 64 && DV == 64 && BC == 64 && !BIAS && !CAUSAL && !SPLIT && !KS2),
                 "8-wave workgroups: head size 128 without bias (key split: no mask), 64 without mask or bias");
@@ -1176,10 +1177,10 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v16: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
+  return "gfx950 fa_fwd v17: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
-         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without mask or bias in fixed MFMA segments (32 at "
-         "head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
+         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without bias (below the diagonal with the causal mask) in fixed MFMA "
+         "segments (32 at head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between, its exponent, exponential and row sum a segment apart), "
          "direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
