@@ -140,8 +140,13 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // B=2, H=32, N=8192 and +3 % at B=1, H=16, Nq=4096, Nk=8192.  With the
   // causal mask (the tiles below the diagonal; causal launches of 8192 rows
   // or more run 8 waves): +4 to +5.5 % at 2048 and 4096 rows, +3 % at head
-  // size 64 and 8192 rows.
-  constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !BIAS) || SEG;
+  // size 64 and 8192 rows.  With a bias at head size 128 (32-key tiles: 16
+  // MFMAs and 16 scores per tile, one score per segment): +9 % with a per-key
+  // bias at B=2, H=16, N=8192 (causal +6 %), +20 % at B=1, H=8, Nq=4096,
+  // Nk=8192.  At head size 64 with a bias (three waves per SIMD) it would
+  // spill 21-29 registers.
+  constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !BIAS) ||
+                            (DQK == 128 && DV == 128 && BC == 32 && BIAS) || SEG;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)) ||
                     (NW == 8 && DQK == 64 && DV == 64 && BC == 64 && !BIAS && !CAUSAL && !SPLIT && !KS2),
                 "8-wave workgroups: head size 128 without bias (key split: no mask), 64 without mask or bias");
@@ -771,27 +776,28 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     constexpr int PF = 3, AHEAD = 2;
     if (j + 3 < n_tiles) tile_to_lds<BC, SWZ_ROW, DQK, NWR>(rk, (j + 3) * BC, kbuf(P ^ 1), wr_u, lane);
     tile_to_lds<BC, SWZ_TR, DV, NWR>(rv, (j + 1) * BC, vbuf(P ^ 1), wr_u, lane);
+    if constexpr (BIAS) load_bias(j + 2, bnext);
     const char* ks = kbuf(P);
     const char* vs = vbuf(P);
     // NS MFMAs of S (m < NS: key block m % KB, k step m / KB), then NP of
     // P V (NS + m: output block m % NCB, keys 16 (m / NCB) .. +15); SPS of
-    // the lane's 32 scores per segment
-    constexpr int NS = KB * NT, NP = NCB * (BC / 16), NM = NS + NP, SPS = 32 / NM;
-    static_assert(KB == 2 && SPS * NM == 32 && (SPS == 1 || SPS % 2 == 0), "segment layout");
+    // the lane's NSC scores per segment
+    constexpr int NS = KB * NT, NP = NCB * (BC / 16), NM = NS + NP, NSC = 16 * KB, SPS = NSC / NM;
+    static_assert(SPS * NM == NSC && (SPS == 1 || SPS % 2 == 0), "segment layout");
     constexpr int CSH = NCB == 4 ? 2 : 1;  // log2(NCB)
     static_assert(NCB == (1 << CSH), "output blocks");
     auto kfrag = [&](int m) FA_INLINE {
       return __builtin_bit_cast(bf16x8,
-                                *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>((m & 1) * 32 + c, 2 * (m >> 1) + h)));
+                                *reinterpret_cast<const uintx4*>(ks + swz<SWZ_ROW, DQK>((m % KB) * 32 + c, 2 * (m / KB) + h)));
     };
     auto vfrag = [&](int m) FA_INLINE {
       return tr_read_a<SWZ_TR, DV>(vs, (uint32_t)((m >> CSH) * 16), m & (NCB - 1), lane);
     };
     floatx16 s2[KB];
-    s2[0] = floatx16{};
-    s2[1] = floatx16{};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s2[kb] = floatx16{};
     bf16x8 kf[PF + 1], vf[PF + 1], pn[2 * KB];
-    float pe[32], xe[32];
+    float pe[NSC], xe[NSC];
     float lsum = 0.0f, lrnd = 0.0f;
     const bf16x2 one{(__bf16)1.0f, (__bf16)1.0f};
     // score r of this lane (key block r >> 4, row r & 15) in three steps, each
@@ -799,13 +805,17 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // the result of the one just issued: the exponent, the exponential, the
     // row sum
     auto st_fma = [&](int r) FA_INLINE {
-      if (r < 32) xe[r] = __builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run);
+      if (r >= NSC) return;
+      if constexpr (BIAS)  // as in the plain iteration's fast path
+        xe[r] = __builtin_fmaf(s1[r >> 4][r & 15], c_log2, bcur[r >> 4][(r & 15) >> 2][r & 3] * LOG2E) - m_run;
+      else
+        xe[r] = __builtin_fmaf(s1[r >> 4][r & 15], c_log2, -m_run);
     };
     auto st_exp = [&](int r) FA_INLINE {
-      if (r < 32) pe[r] = __builtin_amdgcn_exp2f(xe[r]);
+      if (r < NSC) pe[r] = __builtin_amdgcn_exp2f(xe[r]);
     };
     auto st_add = [&](int r) FA_INLINE {
-      if (r < 32) lsum += pe[r];
+      if (r < NSC) lsum += pe[r];
     };
     auto pack = [&](int q) FA_INLINE {  // scores 2q, 2q + 1 -> bf16 (RNE), and their rounded sum
       const int r = 2 * q;
@@ -841,7 +851,7 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
         for (int u = 0; u < SPS / 2; ++u) pack(i * (SPS / 2) + u);
       }
       if (i < NS) {
-        s2[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qb[i >> 1], s2[i & 1], 0, 0, 0);
+        s2[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qb[i / KB], s2[i % KB], 0, 0, 0);
       } else {
         const int m = i - NS;
         oacc[m & (NCB - 1)] =
@@ -859,7 +869,8 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     keep(lrnd);
     float alpha = 1.0f;
     if (fix) {
-      alpha = softmax_fix(s1, pn, lsum, lrnd);
+      if constexpr (BIAS) alpha = softmax_fix_logits(s1, bcur, pn, lsum, lrnd);
+      else alpha = softmax_fix(s1, pn, lsum, lrnd);
       rescale_o(alpha);
     }
     l_run = l_run * alpha + lsum;
@@ -868,8 +879,14 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     keep(l_rnd);
 #pragma unroll
     for (int i = 0; i < 2 * KB; ++i) pb[i] = pn[i];
-    s1[0] = s2[0];
-    s1[1] = s2[1];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s1[kb] = s2[kb];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bcur[kb][g] = bnext[kb][g];
+    }
     wait_vmem();
     __syncthreads();
     }
@@ -1177,10 +1194,10 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v17: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
+  return "gfx950 fa_fwd v18: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
-         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles without bias (below the diagonal with the causal mask) in fixed MFMA "
-         "segments (32 at head size 128, 16 at 64), BC=64 (32 with bias), 3-stage K/V pipeline "
+         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles (below the diagonal with the causal mask; with a bias at head size 128 "
+         "only) in fixed MFMA segments (32 at head size 128, 16 at 64 and at 128 with a bias), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between, its exponent, exponential and row sum a segment apart), "
          "direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
