@@ -49,18 +49,19 @@ DEFAULT_WORKLOAD = "b2_h16_n8192"
 # bias kernel and the key split; the 8-wave kernel that the default workload
 # runs compiles to the same machine code as when it was measured.)
 MEASURED_TRAFFIC = {
-    "kernel": "gfx950 fa_fwd v18: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 "
+    "kernel": "gfx950 fa_fwd v19: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 "
               "without mask or bias on grids of >= 256 workgroups incl. key-split ranges without mask, causal from "
               "8192 rows; 8 waves as two key groups of 4 on 128 rows, merged in LDS, where 128-row workgroups give "
-              "each CU one), plain tiles (below the diagonal with the causal mask; with a bias at head size 128 "
-              "only) in fixed MFMA segments (32 at head size 128, 16 at 64 and at 128 with a bias), BC=64 (32 with "
-              "bias), 3-stage K/V pipeline (S two tiles ahead of P V, softmax in between, its exponent, "
-              "exponential and row sum a segment apart), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 (K "
-              "fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three "
-              "waves per SIMD and a two-FMA exponent at head size 64 with a bias), V^T via ds_read_b64_tr_b16; O "
-              "divided by the sum of the bf16 P taken on mfma_f32_16x16x32_bf16 with a 0/1 mask (bf16 dot products "
-              "at head size 256 with a bias and (192, 128) without mask or bias); no tile max unless exp2 exceeds "
-              "2^16; causal tile skipping; fp32 additive bias; key split with LSE merge",
+              "each CU one), plain tiles (below the diagonal with the causal mask; with a bias not at head size "
+              "64, (192, 128) causal only with a bias) in fixed MFMA segments (32 at head sizes 128 and 256, 40 at "
+              "(192, 128), 16 at 64 and at 128 with a bias, 20 at (192, 128) with a bias), BC=64 (32 with bias), "
+              "3-stage K/V pipeline (S two tiles ahead of P V, softmax in between, its exponent, exponential and "
+              "row sum a segment apart), direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 (K fragments read two "
+              "k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves per SIMD and a "
+              "two-FMA exponent at head size 64 with a bias), V^T via ds_read_b64_tr_b16; O divided by the sum of "
+              "the bf16 P taken on mfma_f32_16x16x32_bf16 with a 0/1 mask (bf16 dot products at head size 256 with "
+              "a bias and (192, 128) without mask or bias); no tile max unless exp2 exceeds 2^16; causal tile "
+              "skipping; fp32 additive bias; key split with LSE merge",
     "workload": "b2_h16_n8192",
     "bytes": 269.8e6,
     "profile": "profiles/fa_fwd_kernel__b2_h16_n8192__hbm_bytes.txt",

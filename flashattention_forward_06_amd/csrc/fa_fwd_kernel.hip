@@ -144,9 +144,15 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   // MFMAs and 16 scores per tile, one score per segment): +9 % with a per-key
   // bias at B=2, H=16, N=8192 (causal +6 %), +20 % at B=1, H=8, Nq=4096,
   // Nk=8192.  At head size 64 with a bias (three waves per SIMD) it would
-  // spill 21-29 registers.
+  // spill 21-29 registers.  Head sizes 192 and 256 have no whole number of
+  // scores per segment (32 over 40 segments, 16 over 32): the scores are
+  // spread as evenly as whole scores allow.  (192, 128): +7.6 % at B=2, H=16,
+  // N=8192, +16 % with a per-key bias, +20 % causal with it; causal without
+  // a bias (64-key tiles) it spills 37 registers (-12 %) and keeps the plain
+  // iteration.  256: +30 % (causal +28 %), +14 % with a bias (causal +37 %).
   constexpr bool SEG_ITER = (((DQK == 64 && DV == 64) || (DQK == 128 && DV == 128)) && BC == 64 && !BIAS) ||
-                            (DQK == 128 && DV == 128 && BC == 32 && BIAS) || SEG;
+                            (DQK == 128 && DV == 128 && BC == 32 && BIAS) || (DQK == 192 && DV == 128 && (BIAS || !CAUSAL)) ||
+                            (DQK == 256 && DV == 256) || SEG;
   static_assert(NW == 4 || (NW == 8 && DQK == 128 && DV == 128 && BC == 64 && !BIAS && !(SPLIT && CAUSAL)) ||
                     (NW == 8 && DQK == 64 && DV == 64 && BC == 64 && !BIAS && !CAUSAL && !SPLIT && !KS2),
                 "8-wave workgroups: head size 128 without bias (key split: no mask), 64 without mask or bias");
@@ -783,8 +789,10 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     // P V (NS + m: output block m % NCB, keys 16 (m / NCB) .. +15); SPS of
     // the lane's NSC scores per segment
     constexpr int NS = KB * NT, NP = NCB * (BC / 16), NM = NS + NP, NSC = 16 * KB, SPS = NSC / NM;
-    static_assert(SPS * NM == NSC && (SPS == 1 || SPS % 2 == 0), "segment layout");
-    constexpr int CSH = NCB == 4 ? 2 : 1;  // log2(NCB)
+    // SPS_INT: SPS scores in every segment; else segment v's scores are
+    // [sc0(v), sc0(v + 1)), spread as evenly as whole scores allow
+    constexpr bool SPS_INT = SPS >= 1 && SPS * NM == NSC && (SPS == 1 || SPS % 2 == 0);
+    constexpr int CSH = NCB == 8 ? 3 : (NCB == 4 ? 2 : 1);  // log2(NCB)
     static_assert(NCB == (1 << CSH), "output blocks");
     auto kfrag = [&](int m) FA_INLINE {
       return __builtin_bit_cast(bf16x8,
@@ -824,14 +832,15 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       pn[r >> 3][(r & 7) + 1] = pr[1];
       if constexpr (!RSUM_MFMA) lrnd = __builtin_amdgcn_fdot2_f32_bf16(pr, one, lrnd, false);
     };
+    auto sc0 = [](int v) FA_INLINE { return v <= 0 ? 0 : (v >= NM ? NSC : v * NSC / NM); };
 #pragma unroll
     for (int i = 0; i < PF; ++i) kf[i] = kfrag(i);
 #pragma unroll
-    for (int r = 0; r < SPS * (AHEAD + 1); ++r) st_fma(r);
+    for (int r = 0; r < sc0(AHEAD + 1); ++r) st_fma(r);
 #pragma unroll
-    for (int r = 0; r < SPS * AHEAD; ++r) st_exp(r);
+    for (int r = 0; r < sc0(AHEAD); ++r) st_exp(r);
 #pragma unroll
-    for (int r = 0; r < SPS * (AHEAD - 1); ++r) st_add(r);
+    for (int r = 0; r < sc0(AHEAD - 1); ++r) st_add(r);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -839,16 +848,20 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
       if (nxt < NS) kf[nxt % (PF + 1)] = kfrag(nxt);
       else if (nxt < NM) vf[(nxt - NS) % (PF + 1)] = vfrag(nxt - NS);
 #pragma unroll
-      for (int u = 0; u < SPS; ++u) st_fma(SPS * (i + AHEAD + 1) + u);
+      for (int r = sc0(i + AHEAD + 1); r < sc0(i + AHEAD + 2); ++r) st_fma(r);
 #pragma unroll
-      for (int u = 0; u < SPS; ++u) st_exp(SPS * (i + AHEAD) + u);
+      for (int r = sc0(i + AHEAD); r < sc0(i + AHEAD + 1); ++r) st_exp(r);
 #pragma unroll
-      for (int u = 0; u < SPS; ++u) st_add(SPS * (i + AHEAD - 1) + u);
-      if constexpr (SPS == 1) {
+      for (int r = sc0(i + AHEAD - 1); r < sc0(i + AHEAD); ++r) st_add(r);
+      if constexpr (SPS_INT && SPS == 1) {
         if (i & 1) pack(i >> 1);
-      } else {
+      } else if constexpr (SPS_INT) {
 #pragma unroll
         for (int u = 0; u < SPS / 2; ++u) pack(i * (SPS / 2) + u);
+      } else {
+        // the pairs whose exponentials were all taken before this segment
+#pragma unroll
+        for (int q = sc0(i + AHEAD - 1) / 2; q < sc0(i + AHEAD) / 2; ++q) pack(q);
       }
       if (i < NS) {
         s2[i % KB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i % (PF + 1)], qb[i / KB], s2[i % KB], 0, 0, 0);
@@ -1194,10 +1207,11 @@ int launch_fa_fwd(const LaunchArgs& a, hipStream_t stream) {
 }
 
 const char* kernel_config_string() {
-  return "gfx950 fa_fwd v18: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
+  return "gfx950 fa_fwd v19: BR=128 (4 waves x 32 rows; 256 = 8 waves for head size 128 without bias and 64 without mask or bias on grids of "
          ">= 256 workgroups incl. key-split ranges without mask, causal from 8192 rows; 8 waves as two key groups "
-         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles (below the diagonal with the causal mask; with a bias at head size 128 "
-         "only) in fixed MFMA segments (32 at head size 128, 16 at 64 and at 128 with a bias), BC=64 (32 with bias), 3-stage K/V pipeline "
+         "of 4 on 128 rows, merged in LDS, where 128-row workgroups give each CU one), plain tiles (below the diagonal with the causal mask; with a bias not at head size 64, "
+         "(192, 128) causal only with a bias) in fixed MFMA segments (32 at head sizes 128 and 256, 40 at (192, 128), 16 "
+         "at 64 and at 128 with a bias, 20 at (192, 128) with a bias), BC=64 (32 with bias), 3-stage K/V pipeline "
          "(S two tiles ahead of P V, softmax in between, its exponent, exponential and row sum a segment apart), "
          "direct-to-LDS, S^T=K.Q^T on mfma_f32_32x32x16_bf16 "
          "(K fragments read two k steps ahead at head size 128, one at (192, 128) without mask or bias; three waves "
