@@ -766,16 +766,18 @@ fa_fwd_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
   };
 
   // Iteration j on a plain tile with SEG_ITER: the same three pieces of work as
-  // `iteration`, in a fixed order of 32 scheduling segments, one MFMA each:
-  // the 16 MFMAs of S(j+2), then the 16 of P(j) V(j) (those run on the V
-  // buffer the copies of this iteration do not touch, and start late, after
-  // the copies have had half an iteration).  Segment i also reads the LDS
-  // operand of the MFMA PF segments later (a ring of PF + 1 fragments per
-  // product) and computes score i + AHEAD of the softmax of tile j+1, which
-  // gives every MFMA about four VALU instructions of the same wave: about as
-  // much VALU work as an MFMA hides (an exponential costs four FMAs, and
-  // about 8 VALU cycles fit under one 32-cycle MFMA).  The compiler still
-  // places the LDS waits, each for a read PF segments old.
+  // `iteration`, in a fixed order of scheduling segments, one MFMA each (32 at
+  // head size 128 with 64-key tiles): the MFMAs of S(j+2), then those of
+  // P(j) V(j) (those run on the V buffer the copies of this iteration do not
+  // touch, and start late, after the copies have had half an iteration).
+  // Segment i also reads the LDS operand of the MFMA PF segments later (a ring
+  // of PF + 1 fragments per product) and advances the softmax of tile j+1:
+  // the exponent of its scores of segment i + AHEAD + 1, the exponentials of
+  // those of i + AHEAD and the row-sum adds of those of i + AHEAD - 1, each
+  // step on results of the segment before, so that none waits for the
+  // instruction just issued.  That is about four VALU instructions per MFMA:
+  // about as much VALU work as an MFMA hides.  The compiler still places the
+  // LDS waits, each for a read PF segments old.
   auto iteration_seg = [&](int j, auto par_tag) FA_INLINE {
     if constexpr (SEG_ITER) {
     constexpr int P = decltype(par_tag)::value;
